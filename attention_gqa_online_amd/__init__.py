@@ -1,0 +1,177 @@
+"""Fused grouped-query attention on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libattn.so`` (declared in ``include/attn.h``). The
+functions carry the C entry points' names and arguments; this module only
+turns torch tensors into device pointers, picks the current HIP stream, and
+raises on a non-OK status. Every step of the computation runs in the HIP
+kernels; there is no other code path. If the library has not been built the
+import still succeeds, but the first call raises.
+
+    attn_prefill_causal(q, k, v, o, m, q_stride, kv_stride, num_q_heads,
+                        heads_per_kv, head_dim, stream=None)
+    attn_decode_workspace_bytes(batch, num_heads, kv_heads, head_dim,
+                                total_seq, window) -> int
+    attn_decode(q, k_cache, v_cache, out, batch, num_heads, kv_heads, head_dim,
+                max_seq, total_seq, window, scale, workspace,
+                workspace_bytes=None, stream=None)
+    kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads, head_dim,
+              max_seq, position, stream=None)
+    attn_status_string(status) -> str
+
+Tensor arguments may be torch tensors (their ``data_ptr()`` is passed, and
+their size is checked against the stated shape) or plain integer device
+addresses (passed as they are).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "AttnError", "ATTN_OK", "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED",
+    "ATTN_ERR_HIP", "SO_PATH", "library", "attn_prefill_causal",
+    "attn_decode_workspace_bytes", "attn_decode", "kv_append",
+    "attn_status_string", "decode_workspace",
+]
+
+SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+
+EXPORTS = ("attn_prefill_causal", "attn_decode_workspace_bytes", "attn_decode",
+           "kv_append", "attn_status_string")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func}: {attn_status_string(status)} (status {status})")
+
+
+_lib = None
+_u32 = ctypes.c_uint32
+_vp = ctypes.c_void_p
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO_PATH):
+            raise RuntimeError(
+                f"{SO_PATH} is missing: build it with "
+                "`python -m attention_gqa_online_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(SO_PATH)
+        lib.attn_prefill_causal.restype = ctypes.c_int
+        lib.attn_prefill_causal.argtypes = [_vp, _vp, _vp, _vp, _u32, _u32, _u32,
+                                            _u32, _u32, _u32, _vp]
+        lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_decode_workspace_bytes.argtypes = [_u32] * 6
+        lib.attn_decode.restype = ctypes.c_int
+        lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32,
+                                    _u32, _u32, _u32, ctypes.c_float, _vp,
+                                    ctypes.c_size_t, _vp]
+        lib.kv_append.restype = ctypes.c_int
+        lib.kv_append.argtypes = [_vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32,
+                                  _u32, _vp]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _ptr(x, name: str, min_elems: int = 0):
+    """Device address of a torch tensor (size-checked) or an int address."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor or an int address")
+    if x.dtype != torch.float32 and name != "workspace":
+        raise TypeError(f"{name}: expected float32, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if x.numel() < min_elems:
+        raise ValueError(f"{name}: has {x.numel()} elements, needs {min_elems}")
+    return x.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(func: str, status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(func, status)
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+def attn_prefill_causal(q, k, v, o, m, q_stride, kv_stride, num_q_heads,
+                        heads_per_kv, head_dim, stream=None) -> None:
+    """Causal GQA prefill; Q/O ``[m, q_stride]``, K/V ``[m, kv_stride]``."""
+    st = library().attn_prefill_causal(
+        _ptr(q, "q", m * q_stride), _ptr(k, "k", m * kv_stride),
+        _ptr(v, "v", m * kv_stride), _ptr(o, "o", m * q_stride),
+        m, q_stride, kv_stride, num_q_heads, heads_per_kv, head_dim,
+        _stream(stream))
+    _check("attn_prefill_causal", st)
+
+
+def attn_decode_workspace_bytes(batch, num_heads, kv_heads, head_dim,
+                                total_seq, window) -> int:
+    return int(library().attn_decode_workspace_bytes(
+        batch, num_heads, kv_heads, head_dim, total_seq, window))
+
+
+def decode_workspace(batch, num_heads, kv_heads, head_dim, total_seq, window,
+                     device=None):
+    """A zero-filled uint8 workspace tensor sized for these decode shapes."""
+    import torch
+    n = attn_decode_workspace_bytes(batch, num_heads, kv_heads, head_dim,
+                                    total_seq, window)
+    if n == 0:
+        raise ValueError("invalid decode shapes")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def attn_decode(q, k_cache, v_cache, out, batch, num_heads, kv_heads, head_dim,
+                max_seq, total_seq, window, scale, workspace,
+                workspace_bytes=None, stream=None) -> None:
+    """Single-query GQA decode with optional sliding window."""
+    n_cache = batch * kv_heads * max_seq * head_dim
+    if workspace_bytes is None:
+        import torch
+        if not isinstance(workspace, torch.Tensor):
+            raise ValueError("workspace_bytes is required for an int workspace")
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = library().attn_decode(
+        _ptr(q, "q", batch * num_heads * head_dim), _ptr(k_cache, "k_cache", n_cache),
+        _ptr(v_cache, "v_cache", n_cache), _ptr(out, "out", batch * num_heads * head_dim),
+        batch, num_heads, kv_heads, head_dim, max_seq, total_seq, window,
+        float(scale), _ptr(workspace, "workspace"), int(workspace_bytes),
+        _stream(stream))
+    _check("attn_decode", st)
+
+
+def kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads, head_dim,
+              max_seq, position, stream=None) -> None:
+    """Write the new K and V rows of every (sequence, KV head) at ``position``."""
+    n_src = batch * kv_heads * head_dim
+    n_cache = batch * kv_heads * max_seq * head_dim
+    st = library().kv_append(
+        _ptr(k_src, "k_src", n_src), _ptr(v_src, "v_src", n_src),
+        _ptr(k_cache, "k_cache", n_cache), _ptr(v_cache, "v_cache", n_cache),
+        batch, kv_heads, head_dim, max_seq, position, _stream(stream))
+    _check("kv_append", st)

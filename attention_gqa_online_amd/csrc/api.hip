@@ -1,0 +1,98 @@
+// C ABI of libattn.so (declared in include/attn.h): argument checks on the
+// host, then one kernel launch on the caller's stream. No check below makes a
+// HIP call, so an invalid call returns before touching the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+bool head_dim_multiple_of_32(uint32_t d) { return d != 0 && d % 32 == 0; }
+bool head_dim_built(uint32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(attn_status s) {
+    switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID: return "ATTN_ERR_INVALID: argument breaks the attn.h contract";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: valid but not built (head_dim)";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime refused the launch";
+    }
+    return "unknown attn_status";
+}
+
+attn_status attn_prefill_causal(const float *q, const float *k, const float *v, float *o,
+                                uint32_t m, uint32_t q_stride, uint32_t kv_stride,
+                                uint32_t num_q_heads, uint32_t heads_per_kv,
+                                uint32_t head_dim, hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim) || heads_per_kv == 0) return ATTN_ERR_INVALID;
+    if (num_q_heads % heads_per_kv != 0) return ATTN_ERR_INVALID;
+    const uint64_t kv_heads = num_q_heads / heads_per_kv;
+    if ((uint64_t)q_stride < (uint64_t)num_q_heads * head_dim) return ATTN_ERR_INVALID;
+    if ((uint64_t)kv_stride < kv_heads * head_dim) return ATTN_ERR_INVALID;
+    if (q_stride % 4 != 0 || kv_stride % 4 != 0) return ATTN_ERR_INVALID;
+    if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (m == 0 || num_q_heads == 0) return ATTN_OK;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID;
+    // grid = kv_heads * ceil(heads_per_kv * ceil(m/32) / 8) workgroups
+    const uint64_t pairs = (uint64_t)heads_per_kv * ((m + 31u) / 32u);
+    if (kv_heads * ((pairs + 7) / 8) > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    return from_hip(attn::launch_prefill(q, k, v, o, m, q_stride, kv_stride, num_q_heads,
+                                         heads_per_kv, head_dim, stream));
+}
+
+size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
+                                   uint32_t head_dim, uint32_t total_seq, uint32_t window) {
+    if (!head_dim_multiple_of_32(head_dim) || !head_dim_built(head_dim)) return 0;
+    if (kv_heads == 0 || num_heads % kv_heads != 0 || total_seq == 0) return 0;
+    if (batch == 0 || num_heads == 0) return 0;
+    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return 0;
+    return attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window)
+        .workspace_bytes;
+}
+
+attn_status attn_decode(const float *q, const float *k_cache, const float *v_cache, float *out,
+                        uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
+                        uint32_t head_dim, uint32_t max_seq, uint32_t total_seq,
+                        uint32_t window, float scale, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
+    if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
+    if (total_seq == 0 || total_seq > max_seq) return ATTN_ERR_INVALID;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 || num_heads == 0) return ATTN_OK;
+    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return ATTN_ERR_INVALID;
+    const attn::DecodePlan plan =
+        attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window);
+    if (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_INVALID;
+    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, batch, num_heads,
+                                        kv_heads, head_dim, max_seq, total_seq, scale,
+                                        workspace, stream));
+}
+
+attn_status kv_append(const float *k_src, const float *v_src, float *k_cache, float *v_cache,
+                      uint32_t batch, uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                      uint32_t position, hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim)) return ATTN_ERR_INVALID;
+    if (position >= max_seq) return ATTN_ERR_INVALID;
+    if (batch == 0 || kv_heads == 0) return ATTN_OK;
+    if ((uint64_t)batch * kv_heads * (head_dim / 4) > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_INVALID;
+    return from_hip(attn::launch_kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads,
+                                           head_dim, max_seq, position, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+// Arguments reaching these functions have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// ---------------------------------------------------------------- decode
+// Work split of one decode call: the attended rows [w0, total_seq) of every
+// (sequence, KV head, head chunk) unit are cut into n_split contiguous row
+// ranges of rows_per_split rows, one workgroup each.
+struct DecodePlan {
+    uint32_t head_chunk;      // Q heads handled per workgroup (<= 8)
+    uint32_t n_chunks;        // head chunks per KV head
+    uint32_t units;           // batch * kv_heads * n_chunks
+    uint32_t n_split;         // workgroups per unit
+    uint32_t rows_per_split;  // multiple of the rows one workgroup step covers
+    uint32_t w0;              // first attended row
+    size_t part_floats;       // partial-state floats in the workspace
+    size_t workspace_bytes;   // partial states + one counter per unit
+};
+
+DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
+                       uint32_t head_dim, uint32_t total_seq, uint32_t window);
+
+hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
+                         const float *v_cache, float *out, uint32_t batch,
+                         uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                         uint32_t max_seq, uint32_t total_seq, float scale,
+                         void *workspace, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+hipError_t launch_prefill(const float *q, const float *k, const float *v, float *o,
+                          uint32_t m, uint32_t q_stride, uint32_t kv_stride,
+                          uint32_t num_q_heads, uint32_t heads_per_kv,
+                          uint32_t head_dim, hipStream_t stream);
+
+// ---------------------------------------------------------------- append
+hipError_t launch_kv_append(const float *k_src, const float *v_src, float *k_cache,
+                            float *v_cache, uint32_t batch, uint32_t kv_heads,
+                            uint32_t head_dim, uint32_t max_seq, uint32_t position,
+                            hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,39 @@
+// KV-cache append of K and V in one launch (glia honeycrisp "attention.rs"
+// page: the KV-append and KV-append-both kernels). Element (b, g, e) of each
+// source row goes to cache[b, g, position, e]; one lane moves 16 bytes of K
+// and 16 bytes of V.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(
+    const float *__restrict__ k_src, const float *__restrict__ v_src, float *__restrict__ k_cache,
+    float *__restrict__ v_cache, uint32_t n4, uint32_t d4, uint32_t max_seq, uint32_t position) {
+    const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= n4) return;
+    const uint32_t bg = idx / d4;  // b * kv_heads + g
+    const uint32_t c = idx % d4;
+    const size_t dst = ((size_t)bg * max_seq + position) * (size_t)(4 * d4) + 4 * c;
+    st4(k_cache + dst, ld4(k_src + 4 * (size_t)idx));
+    st4(v_cache + dst, ld4(v_src + 4 * (size_t)idx));
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const float *k_src, const float *v_src, float *k_cache,
+                            float *v_cache, uint32_t batch, uint32_t kv_heads,
+                            uint32_t head_dim, uint32_t max_seq, uint32_t position,
+                            hipStream_t stream) {
+    const uint32_t d4 = head_dim / 4;
+    const uint32_t n4 = batch * kv_heads * d4;  // bounded by the caller
+    const uint32_t grid = (n4 + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(kThreads), 0, stream, k_src, v_src,
+                       k_cache, v_cache, n4, d4, max_seq, position);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,292 @@
+"""Throughput of the fused GQA attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+                    [--modes headline,decode_window,prefill_long,prefill_qwen,prefill_tiny]
+
+One step = one decode step of the batched-decode workload (32 sequences,
+12 Q / 2 KV heads, head_dim 128, 4096 cached tokens): kv_append of the new
+token's K/V rows at position 4095, then attn_decode over all 4096 positions.
+The timed region holds exactly --steps such steps back to back, bracketed by
+torch.cuda.synchronize(); inputs rotate over three independent cache sets
+(3 x 256 MiB, larger than the 256 MB Infinity Cache) so every step reads its
+K/V from HBM. value = algorithmic K+V bytes per step / step time.
+
+roofline: the decode kernel alone, timed with HIP events recorded around each
+attn_decode call on the stream it is launched on; achieved = algorithmic K+V
+bytes (each attended K and V row read once) / mean event time.
+
+cpu_baseline: the fp64 oracle on this host's cores over the same decode
+workload (all 32 x 12 heads, repeated to >= 10 s).
+
+modes: the other workloads, each timed the same way (median of per-call event
+times): sliding-window decode (GB/s against 8 TB/s HBM), causal prefill
+(TFLOP/s of 2*d*m*(m+1)*Hq against the 157.3 TFLOP/s fp32 matrix peak).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+METRIC = ("decode K/V HBM GB/s (% of 8 TB/s); "
+          "causal prefill fp32 TFLOP/s (% MFMA peak)")
+HEADLINE = "decode_b32_hq12_hkv2_d128_t4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """Hash of the kernel sources; traffic counters are only reported while
+    the kernels are the ones they were measured on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_gqa_online_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel_key)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_calls(fn, n, warmup, stream):
+    """Per-call HIP event times (ms) of fn() on `stream`, plus wall ms/call."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / n
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def bench_headline(args, dev):
+    import numpy as np
+    import torch
+    import attention_gqa_online_amd as A
+    import synth
+
+    w = synth.WORKLOADS[HEADLINE]
+    stream = torch.cuda.current_stream()
+    sets = []
+    for r in range(3):
+        q, k, v = synth.decode_inputs(w, seed=w.seed + r)
+        ks, vs = synth.append_inputs(w.batch, w.kv_heads, w.head_dim, seed=w.seed + 10 + r)
+        sets.append(tuple(torch.from_numpy(x).to(dev) for x in (q, k, v, ks, vs)))
+        if r == 0:
+            host_set0 = (q, k, v)
+    out = torch.empty(w.batch, w.num_heads, w.head_dim, device=dev)
+    ws = A.decode_workspace(w.batch, w.num_heads, w.kv_heads, w.head_dim, w.total_seq,
+                            w.window, device=dev)
+    pos = w.total_seq - 1
+
+    def step(i, ev=None):
+        q, k, v, ks, vs = sets[i % 3]
+        A.kv_append(ks, vs, k, v, w.batch, w.kv_heads, w.head_dim, w.max_seq, pos)
+        if ev is not None:
+            ev[0].record(stream)
+        A.attn_decode(q, k, v, out, w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                      w.max_seq, w.total_seq, w.window, w.scale, ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    mean_kern = statistics.fmean(kern_ms)
+    bytes_ = w.kv_bytes()
+    value = bytes_ / (ms_per_step * 1e-3) / 1e9
+    achieved = bytes_ / (mean_kern * 1e-3) / 1e9
+    log(f"[bench] headline decode: {ms_per_step * 1e3:.1f} us/step, kernel mean "
+        f"{mean_kern * 1e3:.1f} us (min {min(kern_ms) * 1e3:.1f}), {achieved:.0f} GB/s")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("decode_kernel<128, 6, 16, 4>"),
+            "kernel": "decode_kernel<128, 6, 16, 4>",
+            "kernel_mean_us": round(mean_kern * 1e3, 2),
+            "algorithmic_bytes_per_launch": bytes_}
+    return w, value, ms_per_step, roof, host_set0
+
+
+def cpu_baseline(w, host_set):
+    import oracle
+    q, k, v = host_set
+    reps, t_total = 0, 0.0
+    while t_total < 10.0 and reps < 1000:
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, w.batch, w.num_heads, w.kv_heads, w.head_dim, w.max_seq,
+                      w.total_seq, w.window, w.scale)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    gbs = w.kv_bytes() * reps / t_total / 1e9
+    log(f"[bench] cpu oracle: {reps} passes in {t_total:.1f} s, {gbs:.2f} GB/s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole decode workload ({w.batch} sequences x {w.num_heads} heads, "
+                      f"4096 positions), fp64 two-pass softmax, {reps} passes, "
+                      f"{t_total:.1f} s"}
+
+
+def bench_decode_window(args, dev):
+    import torch
+    import attention_gqa_online_amd as A
+    import synth
+    w = synth.WORKLOADS["decode_b16_hq32_hkv8_d128_t32768_w4096"]
+    sets = [synth.decode_inputs_device(w, w.seed + r, dev) for r in range(2)]
+    out = torch.empty(w.batch, w.num_heads, w.head_dim, device=dev)
+    ws = A.decode_workspace(w.batch, w.num_heads, w.kv_heads, w.head_dim, w.total_seq,
+                            w.window, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        q, k, v = sets[i % 2]
+        A.attn_decode(q, k, v, out, w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                      w.max_seq, w.total_seq, w.window, w.scale, ws)
+    ms, wall = time_calls(call, max(args.steps, 10), args.warmup, stream)
+    med = statistics.median(ms)
+    gbs = w.kv_bytes() / (med * 1e-3) / 1e9
+    del sets
+    torch.cuda.empty_cache()
+    log(f"[bench] window decode: median {med * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": w.name, "median_us": round(med * 1e3, 2),
+            "min_us": round(min(ms) * 1e3, 2), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "algorithmic_bytes": w.kv_bytes()}
+
+
+def bench_prefill(args, dev, name, device_inputs=True):
+    import torch
+    import attention_gqa_online_amd as A
+    import synth
+    w = synth.WORKLOADS[name]
+    if device_inputs:
+        q, k, v = synth.prefill_inputs_device(w, w.seed, dev)
+    else:
+        q, k, v = (torch.from_numpy(x).to(dev) for x in synth.prefill_inputs(w))
+    o = torch.empty(w.m, w.q_stride, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        A.attn_prefill_causal(q, k, v, o, w.m, w.q_stride, w.kv_stride, w.num_q_heads,
+                              w.heads_per_kv, w.head_dim)
+    n = max(args.steps, 10) if w.m <= 4096 else max(5, min(args.steps, 10))
+    ms, wall = time_calls(call, n, args.warmup, stream)
+    med = statistics.median(ms)
+    tfl = w.flops() / (med * 1e-3) / 1e12
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    log(f"[bench] {name}: median {med * 1e3:.1f} us, {tfl:.2f} TFLOP/s")
+    return {"workload": name, "median_us": round(med * 1e3, 2),
+            "min_us": round(min(ms) * 1e3, 2), "TFLOP/s": round(tfl, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tfl, 3),
+                         "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tfl / FP32_MFMA_PEAK_TFLOPS, 4)},
+            "algorithmic_flops": w.flops()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--modes", default="headline,decode_window,prefill_long,prefill_qwen,prefill_tiny")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU code; each GPU would run its own share)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_gqa_online_amd as A
+    if not os.path.exists(A.SO_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    A.library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    modes = set(args.modes.split(","))
+
+    w, value, ms_per_step, roof, host_set = bench_headline(args, dev)
+    extra = {}
+    if "decode_window" in modes:
+        extra["decode_window"] = bench_decode_window(args, dev)
+    if "prefill_long" in modes:
+        extra["prefill_long"] = bench_prefill(args, dev, "prefill_hq64_hkv8_d128_m16384")
+    if "prefill_qwen" in modes:
+        extra["prefill_qwen"] = bench_prefill(args, dev, "prefill_hq28_hkv4_d128_m2048")
+    if "prefill_tiny" in modes:
+        extra["prefill_tiny"] = bench_prefill(args, dev, "prefill_hq4_hkv2_d32_m16",
+                                              device_inputs=False)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, host_set)
+
+    props = torch.cuda.get_device_properties(dev)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                   "total_seq": w.total_seq, "window": w.window,
+                   "step": "kv_append + attn_decode", "input_sets": 3},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "modes": extra,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "kernel_sources": source_digest(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * attn.h -- fused grouped-query attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so. Three operations, each one kernel launch:
+ *
+ *   attn_prefill_causal   causal self-attention over a packed projection output
+ *   attn_decode           single-query attention over a KV cache, optional
+ *                         sliding window
+ *   kv_append             write one new K row and V row per (sequence, KV head)
+ *                         into the caches
+ *
+ * Common rules
+ *   - Every tensor is fp32, row-major. Every pointer is a DEVICE pointer owned
+ *     by the caller; the library allocates nothing and keeps no state across
+ *     calls apart from the decode workspace the caller passes in.
+ *   - Grouped-query head map: Q head h reads KV head h / heads_per_kv
+ *     (integer division), so consecutive Q heads share a KV head.
+ *   - Calls are asynchronous on `stream` (0 = the default stream). They
+ *     return after the launch; errors inside the kernel surface at the
+ *     caller's next synchronisation. All argument checks run on the host
+ *     before any HIP call, so an invalid call launches nothing.
+ *   - Outputs must not overlap inputs. Concurrent calls must not share an
+ *     output buffer or a decode workspace.
+ *   - Pointers must be 16-byte aligned; strides are in elements and must be
+ *     multiples of 4 (every row starts 16-byte aligned).
+ *   - head_dim must be a multiple of 32 (ATTN_ERR_INVALID otherwise); this
+ *     build supports head_dim in {32, 64, 128, 256} (ATTN_ERR_UNSUPPORTED for
+ *     the other multiples of 32).
+ *
+ * The softmax is evaluated in one pass with a running maximum, a correction
+ * factor and a running sum (online softmax), so no score matrix is stored;
+ * results match plain softmax attention up to fp32 rounding.
+ */
+#ifndef ATTN_GQA_ATTN_H
+#define ATTN_GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,              /* launched (or nothing to do)                    */
+    ATTN_ERR_INVALID = 1,     /* an argument breaks the contract above          */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid, but outside what this build implements  */
+    ATTN_ERR_HIP = 3          /* the HIP runtime refused the launch             */
+} attn_status;
+
+/*
+ * Causal prefill (aprender-gpu 0.32.0 "prefill_fused.rs" page: the module doc,
+ * the PrefillAttentionKernel constructor and the kernel parameter list).
+ *
+ *   q  [m, q_stride]   Q head h at columns [h*head_dim, (h+1)*head_dim)
+ *   k  [m, kv_stride]  KV head g at columns [g*head_dim, (g+1)*head_dim)
+ *   v  [m, kv_stride]  same layout as k
+ *   o  [m, q_stride]   written at the same columns as q; other columns untouched
+ *
+ * For every Q head h < num_q_heads and row i < m:
+ *   O[i, h] = sum_{j <= i} softmax_j( scale * <Q[i, h], K[j, g]> ) V[j, g],
+ *   g = h / heads_per_kv, scale = 1.0f / sqrtf((float)head_dim).
+ * Rows may be slices of a fused [m, (Hq + 2*Hkv)*head_dim] projection output
+ * (q_stride = kv_stride = that row length, k and v offset into the row).
+ *
+ * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, heads_per_kv == 0,
+ * num_q_heads % heads_per_kv != 0, q_stride < num_q_heads*head_dim,
+ * kv_stride < (num_q_heads/heads_per_kv)*head_dim, a stride not a multiple
+ * of 4, or a null / misaligned pointer. m == 0 or num_q_heads == 0 returns
+ * ATTN_OK without a launch.
+ */
+attn_status attn_prefill_causal(const float *q, const float *k, const float *v,
+                                float *o, uint32_t m, uint32_t q_stride,
+                                uint32_t kv_stride, uint32_t num_q_heads,
+                                uint32_t heads_per_kv, uint32_t head_dim,
+                                hipStream_t stream);
+
+/*
+ * Size in bytes of the decode workspace for these shapes (glia honeycrisp
+ * "attention.rs" page: the decode module doc and its Params struct). Pure
+ * host function; 0 if the shapes are invalid. Any buffer at least this large
+ * serves, provided it was zero-filled before its first use: attn_decode
+ * keeps a per-(sequence, KV head) arrival counter in it and leaves every
+ * counter back at zero when the call completes, so one zeroed workspace can
+ * be reused by any later call (serially, on one stream) whose size fits.
+ */
+size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads,
+                                   uint32_t kv_heads, uint32_t head_dim,
+                                   uint32_t total_seq, uint32_t window);
+
+/*
+ * Single-query decode with optional sliding window (glia honeycrisp
+ * "attention.rs" page: the decode module doc, the Params struct and the
+ * window_start rule of the flash-decode kernel).
+ *
+ *   q        [batch, num_heads, head_dim]
+ *   k_cache  [batch, kv_heads, max_seq, head_dim]   rows >= total_seq unused
+ *   v_cache  same layout as k_cache
+ *   out      [batch, num_heads, head_dim]
+ *
+ * With repeat = num_heads / kv_heads and
+ *   w0 = (window > 0 && total_seq > window) ? total_seq - window : 0,
+ * for every sequence b and head h:
+ *   out[b, h] = sum_{w0 <= s < total_seq}
+ *               softmax_s( scale * <q[b, h], K[b, h/repeat, s]> ) V[b, h/repeat, s].
+ * Rows before w0 are never read. The current token is expected to be in the
+ * cache already (kv_append at position total_seq - 1 first).
+ *
+ * workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
+ * zero-filled before first use (see above). The sequence range is split over
+ * many workgroups; their partial (max, sum, accumulator) states meet in the
+ * workspace and the last workgroup to finish a (sequence, KV head) merges them.
+ *
+ * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, kv_heads == 0,
+ * num_heads % kv_heads != 0, total_seq == 0, total_seq > max_seq,
+ * workspace_bytes too small, scale not finite, or a null / misaligned pointer.
+ * batch == 0 or num_heads == 0 returns ATTN_OK without a launch.
+ */
+attn_status attn_decode(const float *q, const float *k_cache,
+                        const float *v_cache, float *out, uint32_t batch,
+                        uint32_t num_heads, uint32_t kv_heads,
+                        uint32_t head_dim, uint32_t max_seq,
+                        uint32_t total_seq, uint32_t window, float scale,
+                        void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * KV-cache append of K and V in one launch (glia honeycrisp "attention.rs"
+ * page: the KV-append and KV-append-both kernels).
+ *
+ *   k_src, v_src      [batch, kv_heads, head_dim]
+ *   k_cache, v_cache  [batch, kv_heads, max_seq, head_dim]
+ *
+ * k_cache[b, g, position, :] = k_src[b, g, :] and the same for V; no other
+ * element is written. Sources must not overlap the caches.
+ *
+ * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, position >= max_seq, or a
+ * null / misaligned pointer. batch == 0 or kv_heads == 0 returns ATTN_OK
+ * without a launch.
+ */
+attn_status kv_append(const float *k_src, const float *v_src, float *k_cache,
+                      float *v_cache, uint32_t batch, uint32_t kv_heads,
+                      uint32_t head_dim, uint32_t max_seq, uint32_t position,
+                      hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char *attn_status_string(attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_GQA_ATTN_H */

@@ -108,13 +108,17 @@ class Oracle:
     def prefill_causal(self, q, k, v, m, q_stride, kv_stride, num_q_heads,
                        heads_per_kv, head_dim, rows=None, heads=None):
         """Causal GQA prefill in fp64 (all pairs, or the selected (row, head) ones)."""
-        if (q.size < m * q_stride or k.size < m * kv_stride
-                or v.size < m * kv_stride):
-            raise ValueError("input arrays smaller than m * stride")
+        kv_heads = num_q_heads // max(heads_per_kv, 1)
         if num_q_heads * head_dim > q_stride:
             raise ValueError("q_stride too small")
-        if (num_q_heads // max(heads_per_kv, 1)) * head_dim > kv_stride:
+        if kv_heads * head_dim > kv_stride:
             raise ValueError("kv_stride too small")
+        # elements read: rows 0..m-1, columns [0, heads*d) of each row (so a
+        # flat view starting inside a fused projection row is accepted)
+        if m and (q.size < (m - 1) * q_stride + num_q_heads * head_dim
+                  or k.size < (m - 1) * kv_stride + kv_heads * head_dim
+                  or v.size < (m - 1) * kv_stride + kv_heads * head_dim):
+            raise ValueError("input arrays smaller than the rows they must hold")
         rows, heads, n_sel = _sel(rows, heads)
         if rows is None:
             out = np.empty((m, num_q_heads, head_dim), dtype=np.float64)

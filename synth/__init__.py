@@ -181,3 +181,43 @@ def append_inputs(batch: int, kv_heads: int, head_dim: int, seed: int,
     k = normal(rng, (batch, kv_heads, head_dim), sigma)
     v = normal(rng, (batch, kv_heads, head_dim), sigma)
     return k, v
+
+
+# ---------------------------------------------------------------------------
+# On-device generation for timing runs (large caches in milliseconds). Same
+# distributions and layouts as above, drawn with torch's seeded generator on
+# the GPU; these arrays are for throughput measurement, the numpy ones above
+# are what the oracle checks.
+
+def _torch_normal(gen, shape, sigma, device):
+    import torch
+    a = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        a.mul_(sigma)
+    return a
+
+
+def prefill_inputs_device(w: PrefillWorkload, seed: int, device):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    q = _torch_normal(gen, (w.m, w.q_stride), w.sigma, device)
+    k = _torch_normal(gen, (w.m, w.kv_stride), w.sigma, device)
+    v = _torch_normal(gen, (w.m, w.kv_stride), w.sigma, device)
+    return q, k, v
+
+
+def decode_inputs_device(w: DecodeWorkload, seed: int, device):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    q = _torch_normal(gen, (w.batch, w.num_heads, w.head_dim), w.sigma, device)
+    shape = (w.batch, w.kv_heads, w.max_seq, w.head_dim)
+    k = _torch_normal(gen, shape, w.sigma, device)
+    v = _torch_normal(gen, shape, w.sigma, device)
+    if w.spike_frac > 0.0:
+        n_rows = w.batch * w.kv_heads * w.max_seq
+        n_spike = int(math.floor(w.spike_frac * n_rows))
+        rows = torch.randperm(n_rows, generator=gen, device=device)[:n_spike]
+        k.view(n_rows, w.head_dim)[rows] *= w.spike_scale
+    return q, k, v

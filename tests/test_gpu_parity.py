@@ -1,0 +1,366 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bar: max |GPU - oracle| <= 2e-5 * max|V|, with max|V| over the V elements the
+call may attend (all of V's head columns for prefill; rows [w0, T) of every
+cache for decode). kv_append is bit-exact. Inputs come from synth (seeded).
+Full workload sizes are checked element by element where the oracle is fast
+(decode, the two smaller prefills) and on a stated sample of (row, head)
+outputs for the long prefill.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_gqa_online_amd as A
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    A.library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", file=sys.stderr, flush=True)
+
+
+def _err(got, ref):
+    return float(np.abs(got.astype(np.float64) - ref).max()) if ref.size else 0.0
+
+
+def _assert_close(got, ref, vmax, what):
+    err = _err(got, ref)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err <= TOL * vmax, f"{what}: max|err| {err:.3e} > {TOL * vmax:.3e} (max|V| {vmax:.3f})"
+    return err
+
+
+# ------------------------------------------------------------------ decode
+
+def _gpu_decode(dev, w, q, k, v, ws=None, out=None):
+    qd = torch.from_numpy(q).to(dev)
+    kd = torch.from_numpy(k).to(dev)
+    vd = torch.from_numpy(v).to(dev)
+    if out is None:
+        out = torch.full((w.batch, w.num_heads, w.head_dim), float("nan"), device=dev)
+    if ws is None:
+        ws = A.decode_workspace(w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                                w.total_seq, w.window, device=dev)
+    A.attn_decode(qd, kd, vd, out, w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                  w.max_seq, w.total_seq, w.window, w.scale, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _ref_decode(w, q, k, v):
+    return oracle.decode(q, k, v, w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                         w.max_seq, w.total_seq, w.window, w.scale)
+
+
+def _vmax_decode(w, v):
+    return float(np.abs(v[:, :, w.window_start:w.total_seq]).max())
+
+
+def _decode_case(b, hq, hkv, d, max_seq, t, window=0, sigma=1.0, seed=0, **kw):
+    w = synth.DecodeWorkload("case", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=max_seq, total_seq=t, window=window, sigma=sigma,
+                             seed=seed, **kw)
+    return w, synth.decode_inputs(w)
+
+
+@pytest.mark.parametrize("name", ["decode_b32_hq12_hkv2_d128_t4096",
+                                  "decode_b16_hq32_hkv8_d128_t32768_w4096"])
+def test_decode_full_workloads(dev, name):
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.decode_inputs(w)
+    got = _gpu_decode(dev, w, q, k, v)
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), name)
+
+
+DECODE_SWEEP = [
+    # (batch, hq, hkv, d, max_seq, total_seq, window)
+    (1, 1, 1, 32, 8, 1, 0),
+    (2, 4, 2, 32, 70, 65, 0),
+    (3, 8, 8, 64, 130, 129, 0),
+    (2, 6, 2, 64, 300, 257, 31),
+    (1, 12, 2, 128, 1, 1, 0),
+    (2, 12, 2, 128, 5, 3, 0),
+    (2, 12, 2, 128, 64, 63, 0),
+    (2, 12, 2, 128, 600, 511, 0),
+    (2, 12, 2, 128, 600, 513, 0),
+    (1, 12, 2, 128, 5000, 4097, 0),
+    (2, 12, 2, 128, 2000, 1000, 1),
+    (2, 12, 2, 128, 2000, 1000, 999),
+    (2, 12, 2, 128, 2000, 1000, 1000),
+    (2, 12, 2, 128, 2000, 1000, 1005),
+    (2, 12, 2, 128, 2000, 1000, 129),
+    (1, 3, 1, 128, 100, 77, 0),
+    (1, 5, 1, 128, 100, 77, 13),
+    (2, 7, 1, 128, 400, 333, 0),
+    (2, 16, 2, 128, 300, 300, 0),     # 8 Q heads per KV head
+    (1, 9, 1, 128, 200, 150, 0),      # 9 -> two chunks of 5 and 4 heads
+    (1, 24, 2, 128, 200, 190, 0),     # 12 per KV head -> two chunks of 6
+    (1, 16, 1, 64, 300, 299, 0),      # 16 per KV head -> two chunks of 8
+    (2, 4, 4, 256, 300, 200, 0),
+    (1, 8, 1, 256, 500, 480, 100),
+    (1, 2, 1, 32, 20000, 20000, 0),   # many splits
+    (1, 32, 8, 128, 9000, 9000, 4096),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SWEEP, ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_t{}_w{}".format(*c))
+def test_decode_sweep(dev, case):
+    w, (q, k, v) = _decode_case(*case, seed=hash(case) % 1000)
+    got = _gpu_decode(dev, w, q, k, v)
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), str(case))
+
+
+def test_decode_spiky_window(dev):
+    """N(0, 0.5) values with 1% of K rows x8 over all positions: the
+    out-of-window spikes must not leak in, in-window ones stress the max."""
+    w, (q, k, v) = _decode_case(4, 32, 8, 128, 6000, 6000, window=2048, sigma=0.5,
+                                spike_frac=0.01, spike_scale=8.0, seed=44)
+    got = _gpu_decode(dev, w, q, k, v)
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), "spiky")
+
+
+def test_decode_total_seq_one_returns_v_row0(dev):
+    w, (q, k, v) = _decode_case(3, 12, 2, 128, 9, 1, seed=5)
+    got = _gpu_decode(dev, w, q, k, v)
+    rep = w.num_heads // w.kv_heads
+    for b in range(w.batch):
+        for h in range(w.num_heads):
+            assert np.array_equal(got[b, h], v[b, h // rep, 0])
+
+
+def test_decode_large_scores_stay_finite(dev):
+    """Scores far apart (x100 scale): one row dominates, nothing overflows."""
+    w, (q, k, v) = _decode_case(2, 12, 2, 128, 700, 650, seed=6)
+    w = w.with_(scale=float(np.float32(w.scale * 100)))
+    got = _gpu_decode(dev, w, q, k, v)
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), "large scores")
+
+
+def test_decode_deterministic_and_workspace_reused(dev):
+    """Two identical calls give identical bits; one zeroed workspace serves
+    calls of different shapes in turn (every counter is left at zero)."""
+    big = A.attn_decode_workspace_bytes(32, 12, 2, 128, 4096, 0)
+    ws = torch.zeros(big, dtype=torch.uint8, device=dev)
+    w, (q, k, v) = _decode_case(8, 12, 2, 128, 3000, 2900, seed=9)
+    a = _gpu_decode(dev, w, q, k, v, ws=ws)
+    b = _gpu_decode(dev, w, q, k, v, ws=ws)
+    assert np.array_equal(a, b)
+    w2, (q2, k2, v2) = _decode_case(3, 8, 4, 64, 1500, 1400, window=700, seed=10)
+    _assert_close(_gpu_decode(dev, w2, q2, k2, v2, ws=ws), _ref_decode(w2, q2, k2, v2),
+                  _vmax_decode(w2, v2), "reused workspace")
+    _assert_close(_gpu_decode(dev, w, q, k, v, ws=ws), _ref_decode(w, q, k, v),
+                  _vmax_decode(w, v), "reused workspace, first shape again")
+    assert int(ws[: 4 * 64].view(torch.int32).abs().sum()) == 0
+
+
+def test_decode_on_a_side_stream(dev):
+    w, (q, k, v) = _decode_case(2, 12, 2, 128, 500, 500, seed=11)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        out = torch.empty(w.batch, w.num_heads, w.head_dim, device=dev)
+        ws = A.decode_workspace(w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                                w.total_seq, w.window, device=dev)
+        A.attn_decode(qd, kd, vd, out, w.batch, w.num_heads, w.kv_heads, w.head_dim,
+                      w.max_seq, w.total_seq, w.window, w.scale, ws, stream=s)
+    s.synchronize()
+    _assert_close(out.cpu().numpy(), _ref_decode(w, q, k, v), _vmax_decode(w, v), "stream")
+
+
+# --------------------------------------------------------------- kv append
+
+@pytest.mark.parametrize("b,hkv,d,ms,pos", [(1, 1, 32, 1, 0), (2, 2, 128, 16, 15),
+                                            (3, 4, 64, 9, 4), (32, 2, 128, 4096, 4095),
+                                            (2, 8, 256, 40, 0)])
+def test_kv_append_bit_exact(dev, b, hkv, d, ms, pos):
+    ks, vs = synth.append_inputs(b, hkv, d, seed=pos + d)
+    kc = torch.full((b, hkv, ms, d), -7.25, device=dev)
+    vc = torch.full((b, hkv, ms, d), 3.5, device=dev)
+    A.kv_append(torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev), kc, vc,
+                b, hkv, d, ms, pos)
+    torch.cuda.synchronize()
+    kn, vn = kc.cpu().numpy(), vc.cpu().numpy()
+    kr = np.full_like(kn, -7.25)
+    vr = np.full_like(vn, 3.5)
+    oracle.kv_append(ks, vs, kr, vr, b, hkv, d, ms, pos)
+    assert np.array_equal(kn, kr) and np.array_equal(vn, vr)
+
+
+def test_kv_append_full_size_window_workload(dev):
+    """Cache shape of the sliding-window workload (2 GiB per cache): the
+    written row is exact and nothing else changed (checked on the GPU)."""
+    b, hkv, d, ms, pos = 16, 8, 128, 32768, 32767
+    ks, vs = synth.append_inputs(b, hkv, d, seed=12)
+    kc = torch.full((b, hkv, ms, d), 1.25, device=dev)
+    vc = torch.full((b, hkv, ms, d), -2.5, device=dev)
+    A.kv_append(torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev), kc, vc,
+                b, hkv, d, ms, pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc[:, :, pos].cpu().numpy(), ks)
+    assert np.array_equal(vc[:, :, pos].cpu().numpy(), vs)
+    assert int((kc[:, :, :pos] != 1.25).sum()) == 0
+    assert int((vc[:, :, :pos] != -2.5).sum()) == 0
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- prefill
+
+def _gpu_prefill(dev, w, q, k, v, fill=float("nan")):
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    o = torch.full((w.m, w.q_stride), fill, device=dev)
+    A.attn_prefill_causal(qd, kd, vd, o, w.m, w.q_stride, w.kv_stride, w.num_q_heads,
+                          w.heads_per_kv, w.head_dim)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+def _heads(w, o):
+    return o[:, : w.num_q_heads * w.head_dim].reshape(w.m, w.num_q_heads, w.head_dim)
+
+
+def _ref_prefill(w, q, k, v, **kw):
+    return oracle.prefill_causal(q, k, v, w.m, w.q_stride, w.kv_stride, w.num_q_heads,
+                                 w.heads_per_kv, w.head_dim, **kw)
+
+
+def _vmax_prefill(w, v):
+    return float(np.abs(v[:, : w.kv_heads * w.head_dim]).max())
+
+
+@pytest.mark.parametrize("name", ["prefill_hq4_hkv2_d32_m16", "prefill_hq28_hkv4_d128_m2048"])
+def test_prefill_full_workloads(dev, name):
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.prefill_inputs(w)
+    o = _gpu_prefill(dev, w, q, k, v)
+    _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), _vmax_prefill(w, v), name)
+
+
+def test_prefill_long_workload_sampled(dev):
+    """Long prefill (M=16384, 64 Q / 8 KV heads, d=128) at full size. Sample:
+    every row of head 0 and head 63 (first and last KV group), the last 64
+    rows of every head, and 1024 seeded random (row, head) pairs."""
+    w = synth.WORKLOADS["prefill_hq64_hkv8_d128_m16384"]
+    q, k, v = synth.prefill_inputs(w)
+    o = _heads(w, _gpu_prefill(dev, w, q, k, v))
+    rng = np.random.default_rng(2024)
+    rows = [np.arange(w.m), np.arange(w.m)]
+    heads = [np.zeros(w.m, np.int64), np.full(w.m, 63)]
+    last = np.arange(w.m - 64, w.m)
+    for h in range(w.num_q_heads):
+        rows.append(last)
+        heads.append(np.full(64, h))
+    rows.append(rng.integers(0, w.m, 1024))
+    heads.append(rng.integers(0, w.num_q_heads, 1024))
+    rows = np.concatenate(rows)
+    heads = np.concatenate(heads)
+    ref = _ref_prefill(w, q, k, v, rows=rows, heads=heads)
+    _assert_close(o[rows, heads], ref, _vmax_prefill(w, v), "long prefill sample")
+
+
+PREFILL_SWEEP = [
+    # (m, hq, hpk, d)
+    (1, 1, 1, 32), (2, 2, 1, 64), (15, 4, 2, 32), (16, 4, 2, 32), (17, 4, 2, 32),
+    (31, 6, 6, 128), (32, 6, 6, 128), (33, 6, 6, 128), (63, 8, 8, 128),
+    (64, 8, 8, 128), (65, 8, 8, 128), (127, 7, 7, 128), (128, 12, 6, 64),
+    (129, 12, 3, 64), (300, 5, 5, 128), (257, 6, 2, 128), (1000, 8, 4, 128),
+    (200, 3, 1, 256), (100, 16, 8, 256), (450, 10, 5, 32), (97, 9, 9, 64),
+    (1000, 28, 7, 128),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_SWEEP, ids=lambda c: "m{}_hq{}_hpk{}_d{}".format(*c))
+def test_prefill_sweep(dev, case):
+    m, hq, hpk, d = case
+    w = synth.PrefillWorkload("case", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d, kv_stride=(hq // hpk) * d, seed=m + d)
+    q, k, v = synth.prefill_inputs(w)
+    o = _gpu_prefill(dev, w, q, k, v)
+    _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), _vmax_prefill(w, v), str(case))
+
+
+def test_prefill_fused_qkv_buffer(dev):
+    """Q, K, V as column slices of one [m, (Hq + 2 Hkv) d] projection output,
+    O written into its own buffer with the same stride; columns outside the
+    Q heads of O stay untouched."""
+    m, hq, hkv, d = 333, 12, 2, 128
+    stride = (hq + 2 * hkv) * d
+    x = synth.normal(np.random.default_rng(77), (m, stride), 1.0)
+    xd = torch.from_numpy(x).to(dev)
+    o = torch.full((m, stride), 9.0, device=dev)
+    base = xd.data_ptr()
+    A.attn_prefill_causal(base, base + 4 * hq * d, base + 4 * (hq + hkv) * d, o, m,
+                          stride, stride, hq, hq // hkv, d)
+    torch.cuda.synchronize()
+    on = o.cpu().numpy()
+    flat = x.reshape(-1)
+    ref = oracle.prefill_causal(x, flat[hq * d:], flat[(hq + hkv) * d:], m, stride, stride,
+                                hq, hq // hkv, d)
+    vmax = float(np.abs(x[:, (hq + hkv) * d:]).max())
+    _assert_close(on[:, : hq * d].reshape(m, hq, d), ref, vmax, "fused qkv")
+    assert np.all(on[:, hq * d:] == 9.0)
+
+
+def test_prefill_row0_and_determinism(dev):
+    w = synth.PrefillWorkload("case", m=200, num_q_heads=8, heads_per_kv=4, head_dim=128,
+                              q_stride=8 * 128 + 64, kv_stride=2 * 128 + 32, seed=3)
+    q, k, v = synth.prefill_inputs(w)
+    a = _gpu_prefill(dev, w, q, k, v)
+    b = _gpu_prefill(dev, w, q, k, v)
+    assert np.array_equal(a[:, : 8 * 128], b[:, : 8 * 128])
+    ha = _heads(w, a)
+    for h in range(8):
+        g = h // 4
+        np.testing.assert_allclose(ha[0, h], v[0, g * 128:(g + 1) * 128], rtol=0, atol=1e-6)
+    assert np.all(np.isnan(a[:, 8 * 128:]))  # padding columns of O untouched
+
+
+def test_prefill_zero_rows_is_a_no_op(dev):
+    o = torch.full((4, 128), 5.0, device=dev)
+    z = torch.empty(0, device=dev)
+    A.attn_prefill_causal(z, z, z, z, 0, 128, 64, 4, 2, 32)
+    torch.cuda.synchronize()
+    assert torch.all(o == 5.0)
+
+
+def test_cross_mode_prefill_rows_equal_decode(dev):
+    """Append prefill's K/V rows one by one with kv_append, decode with
+    total_seq = i + 1 at prefill's scale: equals prefill row i (both on GPU,
+    both against the oracle's prefill)."""
+    m, hq, hpk, d = 150, 12, 6, 128
+    hkv = hq // hpk
+    w = synth.PrefillWorkload("case", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d, kv_stride=hkv * d, seed=21)
+    q, k, v = synth.prefill_inputs(w)
+    o = _heads(w, _gpu_prefill(dev, w, q, k, v))
+    ref = _ref_prefill(w, q, k, v)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    kc = torch.zeros(1, hkv, m, d, device=dev)
+    vc = torch.zeros(1, hkv, m, d, device=dev)
+    for i in range(m):
+        A.kv_append(kd[i], vd[i], kc, vc, 1, hkv, d, m, i)
+    scale = oracle.prefill_scale(d)
+    ws = A.decode_workspace(1, hq, hkv, d, m, 0, device=dev)
+    vmax = _vmax_prefill(w, v)
+    for i in (0, 1, 63, 64, 149):
+        out = torch.empty(1, hq, d, device=dev)
+        qi = torch.from_numpy(np.ascontiguousarray(q[i].reshape(1, hq, d))).to(dev)
+        A.attn_decode(qi, kc, vc, out, 1, hq, hkv, d, m, i + 1, 0, scale, ws)
+        torch.cuda.synchronize()
+        _assert_close(out.cpu().numpy()[0], ref[i], vmax, f"decode row {i}")
+        _assert_close(o[i], ref[i], vmax, f"prefill row {i}")
