@@ -41,6 +41,30 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// group_sum over N independent values, stage by stage: each DPP move reads a
+// register written N instructions earlier, so no wait states are needed
+// between a write and the DPP read of it.
+template <int G, int N>
+__device__ __forceinline__ void group_sum_n(float (&x)[N]) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    if constexpr (G >= 2) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] += dpp<kDppXor1>(x[i]);
+    }
+    if constexpr (G >= 4) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] += dpp<kDppXor2>(x[i]);
+    }
+    if constexpr (G >= 8) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] += dpp<kDppHalfMirror>(x[i]);
+    }
+    if constexpr (G >= 16) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] += dpp<kDppMirror>(x[i]);
+    }
+}
+
 __device__ __forceinline__ float4 operator*(float4 a, float s) {
     return make_float4(a.x * s, a.y * s, a.z * s, a.w * s);
 }
@@ -49,7 +73,23 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
+// acc + <a, b> as a chain of four FMAs into the running sum
+__device__ __forceinline__ float fma4(float acc, float4 a, float4 b) {
+    acc = __builtin_fmaf(a.x, b.x, acc);
+    acc = __builtin_fmaf(a.y, b.y, acc);
+    acc = __builtin_fmaf(a.z, b.z, acc);
+    return __builtin_fmaf(a.w, b.w, acc);
+}
+
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 __device__ __forceinline__ void st4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+
+// Streaming load (read once): nontemporal hint, so the line is not kept
+// in the caches at the expense of data that is reused.
+__device__ __forceinline__ float4 ld4_stream(const float *p) {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4 *>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
 
 }  // namespace attn

@@ -1,0 +1,377 @@
+// Single-query GQA decode kernel (template). Included by decode.hip, which
+// holds the work plan and the dispatch over head_dim and heads per chunk.
+//
+// What is computed follows the decode module of the glia honeycrisp
+// "attention.rs" page (module doc, Params struct, window_start rule): for each
+// head h, softmax over positions s in [w0, total_seq) of scale * <q[h], K[g, s]>
+// weights the V rows of KV head g = h / repeat.
+//
+// Work decomposition (MI355X design; the page's kernel is one 32-lane SIMD
+// group walking every position of one head in sequence):
+//   unit  = (sequence b, KV head g, chunk of <= 8 Q heads of that group)
+//   split = a contiguous range of attended rows; one workgroup of NW waves
+//   wave  = a contiguous sub-range, streamed RPT = 64/LPR rows per step
+//   lane  = (row slot r, d-chunk c): LPR lanes cover one row's head_dim; lane
+//           c holds float4 chunks c, c+LPR, ... so each global_load_dwordx4
+//           of a row is LPR*16 contiguous bytes.
+// Each K row is read from HBM once and used for all Q heads of the chunk (the
+// GQA reuse the pages leave to L2). Loads run P steps ahead of the arithmetic
+// through a register ring, so every wave keeps P*RPT rows of K and V in
+// flight. The q.K dot of a row is reduced over its LPR lanes with DPP
+// butterflies; every lane keeps its own online-softmax state for its row
+// slot, so a step needs no cross-row reduction. The reference value m of a
+// slot is fixed from its first step instead of being raised row by row: the
+// result acc / l is the same for any m, so the loop carries no rescale (no
+// branch, no multiply of the accumulators); it only tracks the largest
+// score, and the rare wave whose scores climb more than kMaxHeadroom above m
+// re-streams its rows once with m = that maximum.
+// The row slots and waves of a workgroup merge through LDS into one partial
+// state (m, l, acc[d]) per head; the workgroups of a unit merge through the
+// workspace: the last one to arrive (atomic counter) combines every split
+// and writes the normalised output, then resets its counter to zero.
+#pragma once
+
+#include "common.hpp"
+
+namespace attn {
+
+constexpr float kMaxHeadroom = 64.0f;  // log2 units: p = 2^(s - m) <= 2^64
+constexpr float kMinRef = -1.0e30f;    // reference floor for slots with no row
+
+struct DecodeArgs {
+    const float *q;
+    const float *k;
+    const float *v;
+    float *out;
+    float *part;      // [units][n_split][HC][D + 2]: acc[D], m, l
+    uint32_t *count;  // [units]
+    uint32_t num_heads, kv_heads, hpk, n_chunks, max_seq;
+    uint32_t w0, total_seq, n_split, rows_per_split;
+    float qscale;     // scale * log2(e): scores come out in log2 units
+};
+
+template <bool NT>
+__device__ __forceinline__ float4 kv_load(const float *p) {
+    if constexpr (NT) return ld4_stream(p);
+    else return ld4(p);
+}
+
+// Merge modes: last-arriving workgroup merges (agent-scope fences), partial
+// states only (a separate merge kernel combines them), or last arrival with
+// write-through partial stores (timing study).
+enum DecodeMerge {
+    kMergeLastArrival = 0,
+    kMergePartialOnly = 1,
+    kMergeLastArrivalSc1 = 2,
+    kMergeDirect = 3,  // one split per unit: write the normalised output directly
+};
+
+template <int D, int HC, int LPR, int NW, int P, int MERGE = kMergePartialOnly, bool NT = true,
+          bool INTERLEAVE = false>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+    constexpr int VPL = D / LPR;   // floats per lane per row
+    constexpr int NF4 = VPL / 4;   // float4 per lane per row
+    constexpr int RPT = 64 / LPR;  // rows per wave step (row slots)
+    constexpr int NSLOT = NW * RPT;
+    static_assert(VPL % 4 == 0 && LPR * VPL == D, "lane tiling");
+
+    __shared__ float s_acc[NSLOT][HC][D];  // per row slot partial accumulators
+    __shared__ float s_m[NSLOT][HC];
+    __shared__ float s_l[NSLOT][HC];
+    __shared__ float s_f[NSLOT][HC];       // slot weight 2^(m_slot - M)
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+    const int slot = wave * RPT + r;
+
+    const uint32_t split = blockIdx.x % a.n_split;
+    const uint32_t unit = blockIdx.x / a.n_split;
+    const uint32_t chunk = unit % a.n_chunks;
+    const uint32_t bg = unit / a.n_chunks;  // b * kv_heads + g
+    const uint32_t g = bg % a.kv_heads;
+    const uint32_t b = bg / a.kv_heads;
+    const uint32_t hl0 = chunk * HC;
+    const int nh = min(HC, (int)(a.hpk - hl0));
+    const uint32_t h0 = g * a.hpk + hl0;
+
+    // rows of this workgroup, then of this wave: either a contiguous quarter
+    // of the workgroup's range, or every NW-th step of it (INTERLEAVE)
+    const uint32_t ws0 = a.w0 + split * a.rows_per_split;
+    const uint32_t ws1 = min(ws0 + a.rows_per_split, a.total_seq);
+    const uint32_t per_wave = a.rows_per_split / NW;
+    const uint32_t ra = INTERLEAVE ? ws0 + wave * RPT : min(ws0 + wave * per_wave, ws1);
+    const uint32_t rb = INTERLEAVE ? ws1 : min(ra + per_wave, ws1);
+    constexpr uint32_t kStride = INTERLEAVE ? NW * RPT : RPT;  // rows between a wave's steps
+    const uint32_t ntile = rb > ra ? (rb - ra + kStride - 1) / kStride : 0;
+
+    const size_t cache_base = (size_t)bg * a.max_seq * D + 4 * c;
+    const float *kb = a.k + cache_base;
+    const float *vb = a.v + cache_base;
+
+    // Online softmax state of this lane's row slot, per head: reference m,
+    // l = sum 2^(s - m), acc = sum 2^(s - m) V, and the largest score seen.
+    // m is fixed from the slot's first step (floored at kMinRef, so masked
+    // rows, score -inf, give 2^(s - m) = 0 and never NaN) and is not raised
+    // in the loop: exact for any m, and p stays finite while scores stay
+    // below m + kMaxHeadroom. A wave whose scores ever exceed that redoes
+    // its range with m = the true maximum (a second pass that cannot overflow).
+    float m[HC], mx[HC], l[HC];
+    float4 acc[HC][NF4];
+#pragma unroll
+    for (int hh = 0; hh < HC; ++hh) {
+        m[hh] = kMinRef;
+        mx[hh] = kNegInf;
+        l[hh] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NF4; ++t) acc[hh][t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    if (ntile > 0) {
+        // q of every head of the chunk, pre-scaled (zero for heads past nh;
+        // those re-read the last valid head so the load stays in bounds)
+        float4 qv[HC][NF4];
+#pragma unroll
+        for (int hh = 0; hh < HC; ++hh) {
+            const int hq = hh < nh ? hh : nh - 1;
+            const float *qh = a.q + ((size_t)b * a.num_heads + h0 + hq) * D + 4 * c;
+            const float qs = hh < nh ? a.qscale : 0.f;
+#pragma unroll
+            for (int t = 0; t < NF4; ++t) qv[hh][t] = ld4(qh + 4 * LPR * t) * qs;
+        }
+
+        // one row step: scores of `row` from kf, softmax weights, V accumulate.
+        // Rows past rb (only in a range's last step) get score -inf: the
+        // penalty seeds the dot product, so masking costs no extra op.
+        auto step = [&](const float4 (&kf)[NF4], const float4 (&vf)[NF4], uint32_t row) {
+            const float pen = row < rb ? 0.f : kNegInf;
+            float sc[HC];
+#pragma unroll
+            for (int hh = 0; hh < HC; ++hh) {
+                sc[hh] = pen;
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) sc[hh] = fma4(sc[hh], qv[hh][t], kf[t]);
+            }
+            group_sum_n<LPR>(sc);
+#pragma unroll
+            for (int hh = 0; hh < HC; ++hh) {
+                mx[hh] = fmaxf(mx[hh], sc[hh]);
+                const float p = fast_exp2(sc[hh] - m[hh]);
+                l[hh] += p;
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) {
+                    acc[hh][t].x += p * vf[t].x;
+                    acc[hh][t].y += p * vf[t].y;
+                    acc[hh][t].z += p * vf[t].z;
+                    acc[hh][t].w += p * vf[t].w;
+                }
+            }
+        };
+
+        {
+            // ring of P row steps in flight; rows past rb are clamped to rb - 1
+            // (in bounds, masked out of the softmax)
+            float4 kf[P][NF4], vf[P][NF4];
+#pragma unroll
+            for (int s = 0; s < P; ++s) {
+                const size_t off = (size_t)min(ra + s * kStride + r, rb - 1) * D;
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+            }
+            // reference m from the first step's scores
+            {
+                const float pen = ra + r < rb ? 0.f : kNegInf;
+                float sc[HC];
+#pragma unroll
+                for (int hh = 0; hh < HC; ++hh) {
+                    sc[hh] = pen;
+#pragma unroll
+                    for (int t = 0; t < NF4; ++t) sc[hh] = fma4(sc[hh], qv[hh][t], kf[0][t]);
+                }
+                group_sum_n<LPR>(sc);
+#pragma unroll
+                for (int hh = 0; hh < HC; ++hh) m[hh] = fmaxf(sc[hh], kMinRef);
+            }
+            for (uint32_t base = 0; base < ntile; base += P) {
+#pragma unroll
+                for (int s = 0; s < P; ++s) {
+                    const uint32_t row = ra + (base + s) * kStride + r;
+                    step(kf[s], vf[s], row);
+                    // refill this ring slot with the step P ahead
+                    const size_t off = (size_t)min(row + P * kStride, rb - 1) * D;
+#pragma unroll
+                    for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+#pragma unroll
+                    for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+                }
+            }
+        }
+
+        bool ovf = false;
+#pragma unroll
+        for (int hh = 0; hh < HC; ++hh) ovf |= mx[hh] > m[hh] + kMaxHeadroom;
+        if (__any(ovf)) {
+            // rare: redo this wave's range against the exact per-slot maximum
+#pragma unroll
+            for (int hh = 0; hh < HC; ++hh) {
+                m[hh] = fmaxf(mx[hh], kMinRef);
+                l[hh] = 0.f;
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) acc[hh][t] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            for (uint32_t i = 0; i < ntile; ++i) {
+                const uint32_t row = ra + i * kStride + r;
+                const size_t off = (size_t)min(row, rb - 1) * D;
+                float4 kf[NF4], vf[NF4];
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) kf[t] = ld4(kb + off + 4 * LPR * t);
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) vf[t] = ld4(vb + off + 4 * LPR * t);
+                step(kf, vf, row);
+            }
+        }
+    }
+
+    // every row slot of the workgroup lands in LDS
+#pragma unroll
+    for (int hh = 0; hh < HC; ++hh) {
+#pragma unroll
+        for (int t = 0; t < NF4; ++t) st4(&s_acc[slot][hh][4 * (c + LPR * t)], acc[hh][t]);
+        if (c == 0) {
+            s_m[slot][hh] = m[hh];
+            s_l[slot][hh] = l[hh];
+        }
+    }
+    __syncthreads();
+    // slot weights against the workgroup max
+    if (tid < HC) {
+        float M = kNegInf;
+        for (int sl = 0; sl < NSLOT; ++sl) M = fmaxf(M, s_m[sl][tid]);
+        for (int sl = 0; sl < NSLOT; ++sl) {
+            const float ms = s_m[sl][tid];
+            s_f[sl][tid] = ms == kNegInf ? 0.f : fast_exp2(ms - M);
+        }
+        s_m[0][tid] = M;  // slot 0's m is no longer needed
+    }
+    __syncthreads();
+
+    // this workgroup's partial state per head: (acc[d], M, L)
+    float *mypart = a.part + ((size_t)unit * a.n_split + split) * HC * (D + 2);
+    for (int idx = tid; idx < HC * D; idx += NW * 64) {
+        const int hh = idx / D;
+        const int d = idx % D;
+        float x = 0.f;
+#pragma unroll 8
+        for (int sl = 0; sl < NSLOT; ++sl) x += s_acc[sl][hh][d] * s_f[sl][hh];
+        float lsum = 0.f;
+        if (d == 0 || MERGE == kMergeDirect)
+            for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh] * s_f[sl][hh];
+        if constexpr (MERGE == kMergeDirect) {
+            if (hh < nh) a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = x / lsum;
+        } else if constexpr (MERGE == kMergeLastArrivalSc1) {
+            __hip_atomic_store(mypart + hh * (D + 2) + d, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+                __hip_atomic_store(mypart + hh * (D + 2) + D, s_m[0][hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(mypart + hh * (D + 2) + D + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            mypart[hh * (D + 2) + d] = x;
+            if (d == 0) {
+                mypart[hh * (D + 2) + D] = s_m[0][hh];
+                mypart[hh * (D + 2) + D + 1] = lsum;
+            }
+        }
+    }
+    if constexpr (MERGE == kMergePartialOnly || MERGE == kMergeDirect) return;
+
+    // publish; the last workgroup of the unit merges every split
+    if constexpr (MERGE == kMergeLastArrivalSc1)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): write-through stores acknowledged
+    else
+        __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = atomicAdd(a.count + unit, 1u);
+        s_last = prev == a.n_split - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if constexpr (MERGE != kMergeLastArrivalSc1) __threadfence();
+
+    const float *up = a.part + (size_t)unit * a.n_split * HC * (D + 2);
+    for (int idx = tid; idx < nh * D; idx += NW * 64) {
+        const int hh = idx / D;
+        const int d = idx % D;
+        float M = kNegInf;
+        for (uint32_t sp = 0; sp < a.n_split; ++sp)
+            M = fmaxf(M, __hip_atomic_load(up + (sp * HC + hh) * (D + 2) + D, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+        float num = 0.f, den = 0.f;
+        for (uint32_t sp = 0; sp < a.n_split; ++sp) {
+            const float *ps = up + (sp * HC + hh) * (D + 2);
+            const float ms = __hip_atomic_load(ps + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float f = ms == kNegInf ? 0.f : fast_exp2(ms - M);
+            num += __hip_atomic_load(ps + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
+            den += __hip_atomic_load(ps + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
+        }
+        a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = num / den;
+    }
+    if (tid == 0) a.count[unit] = 0;
+}
+
+// Second pass of the two-kernel decode: one workgroup of D threads per
+// (unit, head); thread d folds the n_split partial states (acc[d], m, l) into
+// a running log-sum-exp (M, num, den), eight splits per round so the loads of
+// a round are independent, and writes out = num / den.
+constexpr int kMaxSplit = 1024;
+
+template <int D, int HC>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+    const int tid = threadIdx.x;
+    const uint32_t unit = blockIdx.x / HC;
+    const int hh = blockIdx.x % HC;
+    const uint32_t chunk = unit % a.n_chunks;
+    const uint32_t bg = unit / a.n_chunks;
+    const uint32_t g = bg % a.kv_heads;
+    const uint32_t b = bg / a.kv_heads;
+    const uint32_t hl0 = chunk * HC;
+    if ((int)(a.hpk - hl0) <= hh) return;  // head past this chunk's end
+    const uint32_t h = g * a.hpk + hl0 + hh;
+    const uint32_t ns = a.n_split;
+    constexpr uint32_t SS = HC * (D + 2);  // floats between splits
+    const float *up = a.part + (size_t)unit * ns * SS + hh * (D + 2);
+
+    float M = kNegInf, num = 0.f, den = 0.f;
+    for (uint32_t s0 = 0; s0 < ns; s0 += 8) {
+        float ms[8], ls[8], xs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t sp = min(s0 + i, ns - 1);  // past the end: re-read, weight 0
+            const float *ps = up + (size_t)sp * SS;
+            ms[i] = s0 + i < ns ? ps[D] : kNegInf;
+            ls[i] = ps[D + 1];
+            xs[i] = ps[tid];
+        }
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Mn = fmaxf(Mn, ms[i]);
+        const float c = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+        num *= c;
+        den *= c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = ms[i] == kNegInf ? 0.f : fast_exp2(ms[i] - Mn);
+            num += xs[i] * w;
+            den += ls[i] * w;
+        }
+        M = Mn;
+    }
+    a.out[((size_t)b * a.num_heads + h) * D + tid] = num / den;
+}
+
+}  // namespace attn

@@ -26,6 +26,11 @@ struct DecodePlan {
 DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
                        uint32_t head_dim, uint32_t total_seq, uint32_t window);
 
+struct DecodeArgs;
+DecodeArgs decode_args(const DecodePlan &plan, const float *q, const float *k_cache,
+                       const float *v_cache, float *out, uint32_t num_heads, uint32_t kv_heads,
+                       uint32_t max_seq, uint32_t total_seq, float scale, void *workspace);
+
 hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
                          const float *v_cache, float *out, uint32_t batch,
                          uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,

@@ -140,8 +140,8 @@ def bench_headline(args, dev):
         f"{mean_kern * 1e3:.1f} us (min {min(kern_ms) * 1e3:.1f}), {achieved:.0f} GB/s")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode_kernel<128, 6, 16, 4>"),
-            "kernel": "decode_kernel<128, 6, 16, 4>",
+            "traffic": measured_traffic("attn_decode"),
+            "kernel": "attn_decode (decode_kernel split pass + decode_merge_kernel)",
             "kernel_mean_us": round(mean_kern * 1e3, 2),
             "algorithmic_bytes_per_launch": bytes_}
     return w, value, ms_per_step, roof, host_set0
@@ -224,13 +224,28 @@ def bench_prefill(args, dev, name, device_inputs=True):
             "algorithmic_flops": w.flops()}
 
 
+def copy_calibration(dev, mib=256, reps=3):
+    """A plain device copy of known size, for scaling HBM byte counters: each
+    copy reads and writes exactly `mib` MiB."""
+    import torch
+    src = torch.ones(mib * 2**20 // 4, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read_per_copy": mib * 2**20, "bytes_written_per_copy": mib * 2**20,
+            "copies": reps, "kernel": "torch copy_ (elementwise copy kernel)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--modes", default="headline,decode_window,prefill_long,prefill_qwen,prefill_tiny")
+    ap.add_argument("--modes", default="headline,decode_window,prefill_long,prefill_qwen,prefill_tiny",
+                    help="comma list; the headline decode step always runs "
+                         "(also: copy_calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -259,6 +274,8 @@ def main():
     if "prefill_tiny" in modes:
         extra["prefill_tiny"] = bench_prefill(args, dev, "prefill_hq4_hkv2_d32_m16",
                                               device_inputs=False)
+    if "copy_calibration" in modes:
+        extra["copy_calibration"] = copy_calibration(dev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, host_set)
 
     props = torch.cuda.get_device_properties(dev)

@@ -1,7 +1,8 @@
 /*
  * attn.h -- fused grouped-query attention for AMD Instinct MI355X (gfx950).
  *
- * C ABI of libattn.so. Three operations, each one kernel launch:
+ * C ABI of libattn.so. Three operations (prefill and append are one kernel
+ * launch each; decode is two, ordered on the caller's stream):
  *
  *   attn_prefill_causal   causal self-attention over a packed projection output
  *   attn_decode           single-query attention over a KV cache, optional
@@ -79,11 +80,10 @@ attn_status attn_prefill_causal(const float *q, const float *k, const float *v,
 /*
  * Size in bytes of the decode workspace for these shapes (glia honeycrisp
  * "attention.rs" page: the decode module doc and its Params struct). Pure
- * host function; 0 if the shapes are invalid. Any buffer at least this large
- * serves, provided it was zero-filled before its first use: attn_decode
- * keeps a per-(sequence, KV head) arrival counter in it and leaves every
- * counter back at zero when the call completes, so one zeroed workspace can
- * be reused by any later call (serially, on one stream) whose size fits.
+ * host function; 0 if the shapes are invalid. Any device buffer at least this
+ * large serves; its contents on entry do not matter (no clearing needed) and
+ * are scratch afterwards. Calls that run concurrently need separate
+ * workspaces; calls ordered on one stream may share one.
  */
 size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads,
                                    uint32_t kv_heads, uint32_t head_dim,
@@ -107,10 +107,11 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads,
  * Rows before w0 are never read. The current token is expected to be in the
  * cache already (kv_append at position total_seq - 1 first).
  *
- * workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
- * zero-filled before first use (see above). The sequence range is split over
- * many workgroups; their partial (max, sum, accumulator) states meet in the
- * workspace and the last workgroup to finish a (sequence, KV head) merges them.
+ * workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes
+ * (see above). The attended range is split over many workgroups; each writes
+ * its partial (max, sum, accumulator) state per head into the workspace, and
+ * a second kernel, launched after the first on the same stream, merges the
+ * partial states of every (sequence, head) and writes out.
  *
  * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, kv_heads == 0,
  * num_heads % kv_heads != 0, total_seq == 0, total_seq > max_seq,

@@ -114,6 +114,8 @@ DECODE_SWEEP = [
     (2, 4, 4, 256, 300, 200, 0),
     (1, 8, 1, 256, 500, 480, 100),
     (1, 2, 1, 32, 20000, 20000, 0),   # many splits
+    (64, 8, 4, 128, 300, 300, 0),     # 256 units: one split, output written directly
+    (80, 12, 4, 64, 200, 170, 50),    # 320 units, one split, windowed
     (1, 32, 8, 128, 9000, 9000, 4096),
 ]
 
@@ -152,10 +154,10 @@ def test_decode_large_scores_stay_finite(dev):
 
 
 def test_decode_deterministic_and_workspace_reused(dev):
-    """Two identical calls give identical bits; one zeroed workspace serves
-    calls of different shapes in turn (every counter is left at zero)."""
+    """Two identical calls give identical bits; one workspace, never cleared
+    (filled with NaN bytes up front), serves calls of different shapes."""
     big = A.attn_decode_workspace_bytes(32, 12, 2, 128, 4096, 0)
-    ws = torch.zeros(big, dtype=torch.uint8, device=dev)
+    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device=dev)
     w, (q, k, v) = _decode_case(8, 12, 2, 128, 3000, 2900, seed=9)
     a = _gpu_decode(dev, w, q, k, v, ws=ws)
     b = _gpu_decode(dev, w, q, k, v, ws=ws)
@@ -165,7 +167,6 @@ def test_decode_deterministic_and_workspace_reused(dev):
                   _vmax_decode(w2, v2), "reused workspace")
     _assert_close(_gpu_decode(dev, w, q, k, v, ws=ws), _ref_decode(w, q, k, v),
                   _vmax_decode(w, v), "reused workspace, first shape again")
-    assert int(ws[: 4 * 64].view(torch.int32).abs().sum()) == 0
 
 
 def test_decode_on_a_side_stream(dev):
