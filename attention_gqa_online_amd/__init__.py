@@ -16,6 +16,10 @@ import still succeeds, but the first call raises.
                 workspace_bytes=None, stream=None)
     kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads, head_dim,
               max_seq, position, stream=None)
+    attn_decode_append(q, k_new, v_new, k_cache, v_cache, out, batch,
+                       num_heads, kv_heads, head_dim, max_seq, position,
+                       window, scale, workspace, workspace_bytes=None,
+                       stream=None)
     attn_status_string(status) -> str
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed, and
@@ -31,7 +35,7 @@ __all__ = [
     "AttnError", "ATTN_OK", "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED",
     "ATTN_ERR_HIP", "SO_PATH", "library", "attn_prefill_causal",
     "attn_decode_workspace_bytes", "attn_decode", "kv_append",
-    "attn_status_string", "decode_workspace",
+    "attn_decode_append", "attn_status_string", "decode_workspace",
 ]
 
 SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -39,7 +43,7 @@ SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 
 EXPORTS = ("attn_prefill_causal", "attn_decode_workspace_bytes", "attn_decode",
-           "kv_append", "attn_status_string")
+           "kv_append", "attn_decode_append", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -74,6 +78,10 @@ def library() -> ctypes.CDLL:
         lib.kv_append.restype = ctypes.c_int
         lib.kv_append.argtypes = [_vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32,
                                   _u32, _vp]
+        lib.attn_decode_append.restype = ctypes.c_int
+        lib.attn_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32,
+                                           _u32, _u32, _u32, _u32, ctypes.c_float, _vp,
+                                           ctypes.c_size_t, _vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ctypes.c_int]
         _lib = lib
@@ -176,3 +184,27 @@ def kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads, head_dim,
         _ptr(k_cache, "k_cache", n_cache), _ptr(v_cache, "v_cache", n_cache),
         batch, kv_heads, head_dim, max_seq, position, _stream(stream))
     _check("kv_append", st)
+
+
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, out, batch, num_heads,
+                       kv_heads, head_dim, max_seq, position, window, scale,
+                       workspace, workspace_bytes=None, stream=None) -> None:
+    """Append the current token's K/V rows at ``position`` and decode over
+    ``[w0, position]`` (one decode step)."""
+    n_src = batch * kv_heads * head_dim
+    n_cache = batch * kv_heads * max_seq * head_dim
+    if workspace_bytes is None:
+        import torch
+        if workspace is None:
+            workspace_bytes = 0
+        elif isinstance(workspace, torch.Tensor):
+            workspace_bytes = workspace.numel() * workspace.element_size()
+        else:
+            raise ValueError("workspace_bytes is required for an int workspace")
+    st = library().attn_decode_append(
+        _ptr(q, "q", batch * num_heads * head_dim), _ptr(k_new, "k_new", n_src),
+        _ptr(v_new, "v_new", n_src), _ptr(k_cache, "k_cache", n_cache),
+        _ptr(v_cache, "v_cache", n_cache), _ptr(out, "out", batch * num_heads * head_dim),
+        batch, num_heads, kv_heads, head_dim, max_seq, position, window, float(scale),
+        _ptr(workspace, "workspace"), int(workspace_bytes), _stream(stream))
+    _check("attn_decode_append", st)

@@ -77,9 +77,41 @@ attn_status attn_decode(const float *q, const float *k_cache, const float *v_cac
         attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window);
     if (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_INVALID;
     if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
-    return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, batch, num_heads,
-                                        kv_heads, head_dim, max_seq, total_seq, scale,
-                                        workspace, stream));
+    return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
+                                        head_dim, max_seq, total_seq, scale, workspace,
+                                        nullptr, stream));
+}
+
+attn_status attn_decode_append(const float *q, const float *k_new, const float *v_new,
+                               float *k_cache, float *v_cache, float *out, uint32_t batch,
+                               uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                               uint32_t max_seq, uint32_t position, uint32_t window,
+                               float scale, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
+    if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
+    if (position >= max_seq) return ATTN_ERR_INVALID;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0) return ATTN_OK;
+    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_INVALID;
+    const uint32_t total_seq = position + 1;
+    const attn::DecodePlan plan =
+        attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window, true);
+    attn::DecodeAppend app{k_new, v_new, k_cache, v_cache};
+    if (num_heads == 0) {  // nothing to attend: the append alone
+        return from_hip(attn::launch_kv_append(k_new, v_new, k_cache, v_cache, batch, kv_heads,
+                                               head_dim, max_seq, position, stream));
+    }
+    if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
+    if (plan.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes))
+        return ATTN_ERR_INVALID;
+    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
+                                        head_dim, max_seq, total_seq, scale, workspace, &app,
+                                        stream));
 }
 
 attn_status kv_append(const float *k_src, const float *v_src, float *k_cache, float *v_cache,

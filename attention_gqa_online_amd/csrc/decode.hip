@@ -14,22 +14,25 @@ constexpr int lanes_per_row(int d) { return d == 32 ? 8 : 16; }
 
 // Pass 1 writes one partial state per (unit, split, head); pass 2, ordered
 // after it on the same stream, merges the splits of every (unit, head). With
-// a single split per unit, pass 1 writes the normalised output itself.
+// a single split per unit and no appended row, pass 1 writes the normalised
+// output itself.
 template <int D, int HC>
 hipError_t launch_hc(const DecodeArgs &args, uint32_t units, uint32_t n_split,
                      hipStream_t stream) {
     constexpr int LPR = lanes_per_row(D);
-    if (n_split == 1) {
+    if (n_split == 1 && args.k_new == nullptr) {
         hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeDirect,
                                           true, true>),
                            dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly,
-                                      true, true>),
-                       dim3(units * n_split), dim3(kDecodeWaves * 64), 0, stream, args);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (n_split > 0) {
+        hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch,
+                                          kMergePartialOnly, true, true>),
+                           dim3(units * n_split), dim3(kDecodeWaves * 64), 0, stream, args);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((decode_merge_kernel<D, HC>), dim3(units * HC), dim3(D), 0, stream, args);
     return hipGetLastError();
 }
@@ -55,14 +58,21 @@ inline uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1)
 }  // namespace
 
 DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
-                       uint32_t head_dim, uint32_t total_seq, uint32_t window) {
+                       uint32_t head_dim, uint32_t total_seq, uint32_t window, bool append) {
     DecodePlan p{};
     const uint32_t hpk = num_heads / kv_heads;
     p.n_chunks = ceil_div(hpk, 8);
     p.head_chunk = ceil_div(hpk, p.n_chunks);
     p.units = batch * kv_heads * p.n_chunks;
     p.w0 = (window > 0 && total_seq > window) ? total_seq - window : 0;
-    const uint32_t len = total_seq - p.w0;
+    const uint32_t len = total_seq - p.w0 - (append ? 1 : 0);  // rows of the split pass
+    if (len == 0) {  // only the appended row: no split pass
+        p.n_split = 0;
+        p.rows_per_split = 0;
+        p.part_floats = 0;
+        p.workspace_bytes = 0;
+        return p;
+    }
     const uint32_t rpt = 64 / lanes_per_row((int)head_dim);
     const uint32_t step = kDecodeWaves * rpt;
     const uint32_t max_split = ceil_div(len, (uint64_t)kDecodeWaves * kMinRowsPerWave);
@@ -79,15 +89,16 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     return p;
 }
 
-DecodeArgs decode_args(const DecodePlan &plan, const float *q, const float *k_cache,
-                       const float *v_cache, float *out, uint32_t num_heads, uint32_t kv_heads,
-                       uint32_t max_seq, uint32_t total_seq, float scale, void *workspace) {
+hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
+                         const float *v_cache, float *out, uint32_t num_heads,
+                         uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                         uint32_t total_seq, float scale, void *workspace,
+                         const DecodeAppend *append, hipStream_t stream) {
     DecodeArgs a{};
     a.q = q;
     a.k = k_cache;
     a.v = v_cache;
     a.out = out;
-    a.count = nullptr;
     a.part = static_cast<float *>(workspace);
     a.num_heads = num_heads;
     a.kv_heads = kv_heads;
@@ -95,21 +106,17 @@ DecodeArgs decode_args(const DecodePlan &plan, const float *q, const float *k_ca
     a.n_chunks = plan.n_chunks;
     a.max_seq = max_seq;
     a.w0 = plan.w0;
-    a.total_seq = total_seq;
+    a.total_seq = append ? total_seq - 1 : total_seq;  // end of the split pass
     a.n_split = plan.n_split;
     a.rows_per_split = plan.rows_per_split;
     a.qscale = scale * kLog2e;
-    return a;
-}
-
-hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
-                         const float *v_cache, float *out, uint32_t batch,
-                         uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
-                         uint32_t max_seq, uint32_t total_seq, float scale,
-                         void *workspace, hipStream_t stream) {
-    (void)batch;
-    const DecodeArgs a = decode_args(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
-                                     max_seq, total_seq, scale, workspace);
+    if (append) {
+        a.k_new = append->k_new;
+        a.v_new = append->v_new;
+        a.k_dst = append->k_cache;
+        a.v_dst = append->v_cache;
+        a.position = total_seq - 1;
+    }
     const uint32_t hc = plan.head_chunk, u = plan.units, ns = plan.n_split;
     switch (head_dim) {
     case 32: return launch_d<32>(hc, a, u, ns, stream);

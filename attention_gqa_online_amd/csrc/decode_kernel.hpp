@@ -26,9 +26,13 @@
 // score, and the rare wave whose scores climb more than kMaxHeadroom above m
 // re-streams its rows once with m = that maximum.
 // The row slots and waves of a workgroup merge through LDS into one partial
-// state (m, l, acc[d]) per head; the workgroups of a unit merge through the
-// workspace: the last one to arrive (atomic counter) combines every split
-// and writes the normalised output, then resets its counter to zero.
+// state (m, l, acc[d]) per head, written to the workspace; a second kernel
+// on the same stream folds the partial states of every (unit, head) with a
+// running log-sum-exp and writes the normalised output. When the call also
+// appends the current token (attn_decode_append), the split pass covers the
+// rows before it and the merge kernel folds the new row in as one more
+// partial state, scored from the new K row itself, and writes the new K and
+// V rows into the caches.
 #pragma once
 
 #include "common.hpp"
@@ -44,7 +48,12 @@ struct DecodeArgs {
     const float *v;
     float *out;
     float *part;      // [units][n_split][HC][D + 2]: acc[D], m, l
-    uint32_t *count;  // [units]
+    // fused append (merge kernel only): new rows [B, Hkv, D], or null
+    const float *k_new;
+    const float *v_new;
+    float *k_dst;     // the caches, written at row `position`
+    float *v_dst;
+    uint32_t position;
     uint32_t num_heads, kv_heads, hpk, n_chunks, max_seq;
     uint32_t w0, total_seq, n_split, rows_per_split;
     float qscale;     // scale * log2(e): scores come out in log2 units
@@ -56,18 +65,11 @@ __device__ __forceinline__ float4 kv_load(const float *p) {
     else return ld4(p);
 }
 
-// Merge modes: last-arriving workgroup merges (agent-scope fences), partial
-// states only (a separate merge kernel combines them), or last arrival with
-// write-through partial stores (timing study).
-enum DecodeMerge {
-    kMergeLastArrival = 0,
-    kMergePartialOnly = 1,
-    kMergeLastArrivalSc1 = 2,
-    kMergeDirect = 3,  // one split per unit: write the normalised output directly
-};
+// What the split pass writes: one partial state per (unit, split, head) for
+// the merge kernel, or, with a single split per unit, the normalised output.
+enum DecodeMerge { kMergePartialOnly = 1, kMergeDirect = 3 };
 
-template <int D, int HC, int LPR, int NW, int P, int MERGE = kMergePartialOnly, bool NT = true,
-          bool INTERLEAVE = false>
+template <int D, int HC, int LPR, int NW, int P, int MERGE, bool NT, bool INTERLEAVE>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     constexpr int VPL = D / LPR;   // floats per lane per row
     constexpr int NF4 = VPL / 4;   // float4 per lane per row
@@ -79,7 +81,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     __shared__ float s_m[NSLOT][HC];
     __shared__ float s_l[NSLOT][HC];
     __shared__ float s_f[NSLOT][HC];       // slot weight 2^(m_slot - M)
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -273,12 +274,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh] * s_f[sl][hh];
         if constexpr (MERGE == kMergeDirect) {
             if (hh < nh) a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = x / lsum;
-        } else if constexpr (MERGE == kMergeLastArrivalSc1) {
-            __hip_atomic_store(mypart + hh * (D + 2) + d, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == 0) {
-                __hip_atomic_store(mypart + hh * (D + 2) + D, s_m[0][hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(mypart + hh * (D + 2) + D + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
         } else {
             mypart[hh * (D + 2) + d] = x;
             if (d == 0) {
@@ -287,47 +282,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             }
         }
     }
-    if constexpr (MERGE == kMergePartialOnly || MERGE == kMergeDirect) return;
+}
 
-    // publish; the last workgroup of the unit merges every split
-    if constexpr (MERGE == kMergeLastArrivalSc1)
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): write-through stores acknowledged
-    else
-        __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(a.count + unit, 1u);
-        s_last = prev == a.n_split - 1;
+// Sum over the D threads of a workgroup (D in {32, 64, 128, 256}).
+template <int D>
+__device__ __forceinline__ float block_sum(float x) {
+    constexpr int W = D < 64 ? D : 64;
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, W);
+    if constexpr (D <= 64) {
+        return x;
+    } else {
+        __shared__ float red[D / 64];
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+        __syncthreads();
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) t += red[i];
+        return t;
     }
-    __syncthreads();
-    if (!s_last) return;
-    if constexpr (MERGE != kMergeLastArrivalSc1) __threadfence();
-
-    const float *up = a.part + (size_t)unit * a.n_split * HC * (D + 2);
-    for (int idx = tid; idx < nh * D; idx += NW * 64) {
-        const int hh = idx / D;
-        const int d = idx % D;
-        float M = kNegInf;
-        for (uint32_t sp = 0; sp < a.n_split; ++sp)
-            M = fmaxf(M, __hip_atomic_load(up + (sp * HC + hh) * (D + 2) + D, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-        float num = 0.f, den = 0.f;
-        for (uint32_t sp = 0; sp < a.n_split; ++sp) {
-            const float *ps = up + (sp * HC + hh) * (D + 2);
-            const float ms = __hip_atomic_load(ps + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float f = ms == kNegInf ? 0.f : fast_exp2(ms - M);
-            num += __hip_atomic_load(ps + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
-            den += __hip_atomic_load(ps + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
-        }
-        a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = num / den;
-    }
-    if (tid == 0) a.count[unit] = 0;
 }
 
 // Second pass of the two-kernel decode: one workgroup of D threads per
 // (unit, head); thread d folds the n_split partial states (acc[d], m, l) into
 // a running log-sum-exp (M, num, den), eight splits per round so the loads of
-// a round are independent, and writes out = num / den.
+// a round are independent, and writes out = num / den. With a fused append
+// the new row enters first as the state (m = its score, l = 1, acc = v_new).
 constexpr int kMaxSplit = 1024;
 
 template <int D, int HC>
@@ -347,6 +327,19 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     const float *up = a.part + (size_t)unit * ns * SS + hh * (D + 2);
 
     float M = kNegInf, num = 0.f, den = 0.f;
+    if (a.k_new != nullptr) {
+        const float kn = a.k_new[(size_t)bg * D + tid];
+        const float vn = a.v_new[(size_t)bg * D + tid];
+        const float qd = a.q[((size_t)b * a.num_heads + h) * D + tid] * a.qscale;
+        M = block_sum<D>(qd * kn);  // the new row's score, log2 units
+        num = vn;
+        den = 1.f;
+        if (hl0 + hh == 0) {  // one writer per (sequence, KV head)
+            const size_t dst = ((size_t)bg * a.max_seq + a.position) * D + tid;
+            a.k_dst[dst] = kn;
+            a.v_dst[dst] = vn;
+        }
+    }
     for (uint32_t s0 = 0; s0 < ns; s0 += 8) {
         float ms[8], ls[8], xs[8];
 #pragma unroll

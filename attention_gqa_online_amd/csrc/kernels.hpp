@@ -23,19 +23,25 @@ struct DecodePlan {
     size_t workspace_bytes;   // partial states + one counter per unit
 };
 
+// With `append`, the split pass covers [w0, total_seq - 1) and the last row
+// comes from the new K/V rows instead (n_split may then be 0).
 DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
-                       uint32_t head_dim, uint32_t total_seq, uint32_t window);
+                       uint32_t head_dim, uint32_t total_seq, uint32_t window,
+                       bool append = false);
 
-struct DecodeArgs;
-DecodeArgs decode_args(const DecodePlan &plan, const float *q, const float *k_cache,
-                       const float *v_cache, float *out, uint32_t num_heads, uint32_t kv_heads,
-                       uint32_t max_seq, uint32_t total_seq, float scale, void *workspace);
+// New K/V rows for attn_decode_append: written at `position` = total_seq - 1.
+struct DecodeAppend {
+    const float *k_new;
+    const float *v_new;
+    float *k_cache;
+    float *v_cache;
+};
 
 hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
-                         const float *v_cache, float *out, uint32_t batch,
-                         uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
-                         uint32_t max_seq, uint32_t total_seq, float scale,
-                         void *workspace, hipStream_t stream);
+                         const float *v_cache, float *out, uint32_t num_heads,
+                         uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                         uint32_t total_seq, float scale, void *workspace,
+                         const DecodeAppend *append, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill
 hipError_t launch_prefill(const float *q, const float *k, const float *v, float *o,

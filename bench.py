@@ -4,16 +4,19 @@
                     [--modes headline,decode_window,prefill_long,prefill_qwen,prefill_tiny]
 
 One step = one decode step of the batched-decode workload (32 sequences,
-12 Q / 2 KV heads, head_dim 128, 4096 cached tokens): kv_append of the new
-token's K/V rows at position 4095, then attn_decode over all 4096 positions.
-The timed region holds exactly --steps such steps back to back, bracketed by
+12 Q / 2 KV heads, head_dim 128, 4096 cached tokens): append the new token's
+K/V rows at position 4095 and attend over all 4096 positions, as one
+attn_decode_append call (split pass + merge/append pass). The timed region
+holds exactly --steps such steps back to back, bracketed by
 torch.cuda.synchronize(); inputs rotate over three independent cache sets
 (3 x 256 MiB, larger than the 256 MB Infinity Cache) so every step reads its
 K/V from HBM. value = algorithmic K+V bytes per step / step time.
 
-roofline: the decode kernel alone, timed with HIP events recorded around each
-attn_decode call on the stream it is launched on; achieved = algorithmic K+V
-bytes (each attended K and V row read once) / mean event time.
+roofline: the attn_decode_append call, timed with HIP events recorded around
+each call on the stream it is launched on; achieved = algorithmic K+V bytes
+(each attended K and V row read once) / mean event time. The call is two
+kernels (the split pass and the merge pass); their rocprofv3 durations add up
+to the event time less the gap between them.
 
 cpu_baseline: the fp64 oracle on this host's cores over the same decode
 workload (all 32 x 12 heads, repeated to >= 10 s).
@@ -111,40 +114,83 @@ def bench_headline(args, dev):
                             w.window, device=dev)
     pos = w.total_seq - 1
 
-    def step(i, ev=None):
+    # device addresses and the stream as plain ints: the binding passes them
+    # straight through, so the host side of a step is one ctypes call
+    sint = stream.cuda_stream
+    ptrs = [tuple(x.data_ptr() for x in st) for st in sets]
+    outp, wsp, wsb = out.data_ptr(), ws.data_ptr(), ws.numel()
+
+    def step(i):
+        qp, kp, vp, ksp, vsp = ptrs[i % 3]
+        A.attn_decode_append(qp, ksp, vsp, kp, vp, outp, w.batch, w.num_heads, w.kv_heads,
+                             w.head_dim, w.max_seq, pos, w.window, w.scale, wsp, wsb, stream=sint)
+
+    def two_call_step(i):
         q, k, v, ks, vs = sets[i % 3]
         A.kv_append(ks, vs, k, v, w.batch, w.kv_heads, w.head_dim, w.max_seq, pos)
-        if ev is not None:
-            ev[0].record(stream)
         A.attn_decode(q, k, v, out, w.batch, w.num_heads, w.kv_heads, w.head_dim,
                       w.max_seq, w.total_seq, w.window, w.scale, ws)
-        if ev is not None:
-            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    mean_kern = statistics.fmean(kern_ms)
+    mean_kern = ev0.elapsed_time(ev1) / args.steps  # GPU time per call over the timed region
+    # per-call event times, for the spread (a separate pass)
+    kern_ms, _ = time_calls(step, args.steps, 0, stream)
     bytes_ = w.kv_bytes()
     value = bytes_ / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_ / (mean_kern * 1e-3) / 1e9
-    log(f"[bench] headline decode: {ms_per_step * 1e3:.1f} us/step, kernel mean "
-        f"{mean_kern * 1e3:.1f} us (min {min(kern_ms) * 1e3:.1f}), {achieved:.0f} GB/s")
+    log(f"[bench] headline decode step: {ms_per_step * 1e3:.1f} us/step wall, "
+        f"{mean_kern * 1e3:.1f} us/step by events (per-call median "
+        f"{statistics.median(kern_ms) * 1e3:.1f}, min {min(kern_ms) * 1e3:.1f}), "
+        f"{achieved:.0f} GB/s")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("attn_decode"),
-            "kernel": "attn_decode (decode_kernel split pass + decode_merge_kernel)",
+            "traffic": measured_traffic("attn_decode_append"),
+            "kernel": "attn_decode_append: decode_kernel<128, 6, ...> split pass + "
+                      "decode_merge_kernel<128, 6> merge/append pass",
             "kernel_mean_us": round(mean_kern * 1e3, 2),
+            "per_call_median_us": round(statistics.median(kern_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": bytes_}
-    return w, value, ms_per_step, roof, host_set0
+    # the same step as two calls (kv_append, then attn_decode), for comparison
+    ms2, _ = time_calls(two_call_step, args.steps, args.warmup, stream)
+    two = {"step": "kv_append + attn_decode", "median_us": round(statistics.median(ms2) * 1e3, 2),
+           "GB/s": round(bytes_ / (statistics.median(ms2) * 1e-3) / 1e9, 1)}
+    log(f"[bench] two-call step: median {two['median_us']:.1f} us")
+    # the same step replayed from a captured HIP graph (one graph per input set)
+    graphs = []
+    for i in range(3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qp, kp, vp, ksp, vsp = ptrs[i]
+            A.attn_decode_append(qp, ksp, vsp, kp, vp, outp, w.batch, w.num_heads,
+                                 w.kv_heads, w.head_dim, w.max_seq, pos, w.window, w.scale,
+                                 wsp, wsb)
+        graphs.append(g)
+    for i in range(3):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        graphs[i % 3].replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    gwall = (time.perf_counter() - t0) * 1e3 / args.steps
+    gev = g0.elapsed_time(g1) / args.steps
+    two["graph_replay_us_per_step"] = round(gwall * 1e3, 2)
+    two["graph_replay_event_us_per_step"] = round(gev * 1e3, 2)
+    log(f"[bench] graph replay: {gwall * 1e3:.1f} us/step wall, {gev * 1e3:.1f} us by events")
+    return w, value, ms_per_step, roof, host_set0, two
 
 
 def cpu_baseline(w, host_set):
@@ -263,8 +309,8 @@ def main():
     dev = torch.device("cuda:0")
     modes = set(args.modes.split(","))
 
-    w, value, ms_per_step, roof, host_set = bench_headline(args, dev)
-    extra = {}
+    w, value, ms_per_step, roof, host_set, two = bench_headline(args, dev)
+    extra = {"decode_step_two_calls": two}
     if "decode_window" in modes:
         extra["decode_window"] = bench_decode_window(args, dev)
     if "prefill_long" in modes:
@@ -295,7 +341,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim,
                    "total_seq": w.total_seq, "window": w.window,
-                   "step": "kv_append + attn_decode", "input_sets": 3},
+                   "step": "attn_decode_append (append at 4095 + attend 4096)",
+                   "input_sets": 3},
         "roofline": roof,
         "cpu_baseline": cpu,
         "modes": extra,

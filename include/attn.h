@@ -2,13 +2,15 @@
  * attn.h -- fused grouped-query attention for AMD Instinct MI355X (gfx950).
  *
  * C ABI of libattn.so. Three operations (prefill and append are one kernel
- * launch each; decode is two, ordered on the caller's stream):
+ * launch each; decode is two, ordered on the caller's stream), and the decode
+ * step that combines the last two:
  *
  *   attn_prefill_causal   causal self-attention over a packed projection output
  *   attn_decode           single-query attention over a KV cache, optional
  *                         sliding window
  *   kv_append             write one new K row and V row per (sequence, KV head)
  *                         into the caches
+ *   attn_decode_append    kv_append + attn_decode of the same token, two launches
  *
  * Common rules
  *   - Every tensor is fp32, row-major. Every pointer is a DEVICE pointer owned
@@ -125,6 +127,40 @@ attn_status attn_decode(const float *q, const float *k_cache,
                         uint32_t total_seq, uint32_t window, float scale,
                         void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * One decode step: append the current token's K and V rows, then attend
+ * (the two calls kv_append(position) and attn_decode(total_seq = position + 1)
+ * in one: glia honeycrisp "attention.rs" page, the fused append + decode
+ * kernel's doc, which removes the separate append dispatch and the wait
+ * between the two; rotary embedding is not applied here).
+ *
+ *   q                 [batch, num_heads, head_dim]
+ *   k_new, v_new      [batch, kv_heads, head_dim]   the current token's rows
+ *   k_cache, v_cache  [batch, kv_heads, max_seq, head_dim]
+ *   out               [batch, num_heads, head_dim]
+ *
+ * Writes k_cache[b, g, position, :] = k_new[b, g, :] (same for V) and
+ *   out[b, h] = sum_{w0 <= s <= position} softmax_s( scale * <q[b, h], K[b, h/repeat, s]> )
+ *               V[b, h/repeat, s],   w0 from total_seq = position + 1 as in attn_decode,
+ * where row `position` is the new row. Cache rows other than `position` are
+ * only read. The current token's contribution is computed from k_new/v_new,
+ * not read back from the cache. Sources must not overlap the caches.
+ *
+ * workspace: at least attn_decode_workspace_bytes(batch, num_heads, kv_heads,
+ * head_dim, position + 1, window) bytes, contents irrelevant (may be null
+ * when that size is 0).
+ *
+ * Errors: as attn_decode (with total_seq = position + 1), plus position >=
+ * max_seq. batch == 0 returns ATTN_OK without a launch; num_heads == 0 only
+ * appends.
+ */
+attn_status attn_decode_append(const float *q, const float *k_new, const float *v_new,
+                               float *k_cache, float *v_cache, float *out,
+                               uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
+                               uint32_t head_dim, uint32_t max_seq, uint32_t position,
+                               uint32_t window, float scale, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /*
  * KV-cache append of K and V in one launch (glia honeycrisp "attention.rs"

@@ -152,3 +152,25 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(A, "SO_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         A.library()
+
+
+def _decode_append(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, pos=63, window=0,
+                   scale=0.088, ws=P, ws_bytes=1 << 30, ptrs=(P, P, P, P, P, P)):
+    return lib.attn_decode_append(*ptrs, b, hq, hkv, d, max_seq, pos, window,
+                                  ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+def test_decode_append_argument_rules(lib):
+    assert _decode_append(lib, d=48) == INVALID
+    assert _decode_append(lib, d=160) == UNSUPPORTED
+    assert _decode_append(lib, hkv=0) == INVALID
+    assert _decode_append(lib, hq=12, hkv=5) == INVALID
+    assert _decode_append(lib, pos=64, max_seq=64) == INVALID   # past the cache
+    assert _decode_append(lib, scale=float("nan")) == INVALID
+    assert _decode_append(lib, ptrs=(P, 0, P, P, P, P)) == INVALID
+    assert _decode_append(lib, ptrs=(P, P, P, P + 4, P, P)) == INVALID
+    assert _decode_append(lib, ptrs=(P, P, P, P, P, 0)) == INVALID
+    need = lib.attn_decode_workspace_bytes(2, 12, 2, 128, 64, 0)
+    assert _decode_append(lib, ws_bytes=need // 4) == INVALID
+    assert _decode_append(lib, ws=0) == INVALID
+    assert _decode_append(lib, b=0) == OK                        # no work, no launch

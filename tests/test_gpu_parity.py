@@ -183,6 +183,58 @@ def test_decode_on_a_side_stream(dev):
     _assert_close(out.cpu().numpy(), _ref_decode(w, q, k, v), _vmax_decode(w, v), "stream")
 
 
+# ------------------------------------------------------- decode + append
+
+DECODE_APPEND_CASES = [
+    # (batch, hq, hkv, d, max_seq, position, window)
+    (2, 12, 2, 128, 8, 0, 0),          # first token: nothing cached yet
+    (2, 12, 2, 128, 40, 1, 0),
+    (3, 4, 2, 32, 90, 64, 0),
+    (2, 6, 2, 64, 300, 256, 31),
+    (2, 12, 2, 128, 2000, 999, 1),     # window 1: the new row only
+    (2, 12, 2, 128, 2000, 999, 2),
+    (2, 12, 2, 128, 2000, 999, 5000),  # window past the start: no window
+    (1, 9, 1, 128, 300, 250, 0),       # two head chunks
+    (64, 8, 4, 128, 300, 299, 0),      # 256 units
+    (2, 8, 1, 256, 600, 512, 100),
+    (1, 32, 8, 128, 9000, 8999, 4096),
+]
+
+
+def _decode_append_case(dev, case, seed):
+    b, hq, hkv, d, ms, pos, win = case
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, pos + 1, window=win, seed=seed)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=seed + 1)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    out = torch.full((b, hq, d), float("nan"), device=dev)
+    ws = torch.full((max(1, A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win)),),
+                    0xFF, dtype=torch.uint8, device=dev)
+    A.attn_decode_append(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
+                         torch.from_numpy(vn).to(dev), kd, vd, out, b, hq, hkv, d, ms, pos,
+                         win, w.scale, ws)
+    torch.cuda.synchronize()
+    oracle.kv_append(kn, vn, k, v, b, hkv, d, ms, pos)   # the reference step
+    return w, (q, k, v), out.cpu().numpy(), kd.cpu().numpy(), vd.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", DECODE_APPEND_CASES,
+                         ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_pos{}_w{}".format(*c))
+def test_decode_append_matches_append_then_decode(dev, case):
+    w, (q, k, v), got, kc, vc = _decode_append_case(dev, case, seed=sum(case) % 997)
+    assert np.array_equal(kc, k) and np.array_equal(vc, v)  # only row `position` changed
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), str(case))
+
+
+def test_decode_append_full_decode_workload(dev):
+    """The decode workload's shape (32 x 12 heads, 4096 positions) as a decode
+    step: append at position 4095, attend all 4096 rows."""
+    w0 = synth.WORKLOADS["decode_b32_hq12_hkv2_d128_t4096"]
+    case = (w0.batch, w0.num_heads, w0.kv_heads, w0.head_dim, w0.max_seq, 4095, 0)
+    w, (q, k, v), got, kc, vc = _decode_append_case(dev, case, seed=w0.seed)
+    assert np.array_equal(kc, k) and np.array_equal(vc, v)
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), "decode step")
+
+
 # --------------------------------------------------------------- kv append
 
 @pytest.mark.parametrize("b,hkv,d,ms,pos", [(1, 1, 32, 1, 0), (2, 2, 128, 16, 15),
@@ -365,3 +417,38 @@ def test_cross_mode_prefill_rows_equal_decode(dev):
         torch.cuda.synchronize()
         _assert_close(out.cpu().numpy()[0], ref[i], vmax, f"decode row {i}")
         _assert_close(o[i], ref[i], vmax, f"prefill row {i}")
+
+
+def test_decode_calls_replay_correctly_from_a_hip_graph(dev):
+    """attn_decode_append and attn_decode captured in a HIP graph: every
+    replay, with eager work and synchronisations between replays, gives the
+    same bits as the eager call (the kernels are deterministic)."""
+    b, hq, hkv, d, ms, pos = 4, 12, 2, 128, 1500, 1300
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, pos + 1, seed=31)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=32)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    knd, vnd = torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev)
+    ws = A.decode_workspace(b, hq, hkv, d, pos + 1, 0, device=dev)
+    out_e = torch.empty(b, hq, d, device=dev)
+    out_g = torch.empty(b, hq, d, device=dev)
+    out2_e = torch.empty(b, hq, d, device=dev)
+    out2_g = torch.empty(b, hq, d, device=dev)
+    A.attn_decode_append(qd, knd, vnd, kd, vd, out_e, b, hq, hkv, d, ms, pos, 0, w.scale, ws)
+    A.attn_decode(qd, kd, vd, out2_e, b, hq, hkv, d, ms, pos + 1, 0, w.scale, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.attn_decode_append(qd, knd, vnd, kd, vd, out_g, b, hq, hkv, d, ms, pos, 0, w.scale, ws)
+        A.attn_decode(qd, kd, vd, out2_g, b, hq, hkv, d, ms, pos + 1, 0, w.scale, ws)
+    for rep in range(4):
+        out_g.fill_(float("nan"))
+        out2_g.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep}: attn_decode_append differs"
+        assert torch.equal(out2_g, out2_e), f"replay {rep}: attn_decode differs"
+        assert bool(torch.isfinite(junk))
+    oracle.kv_append(kn, vn, k, v, b, hkv, d, ms, pos)
+    _assert_close(out_e.cpu().numpy(), _ref_decode(w.with_(total_seq=pos + 1), q, k, v),
+                  _vmax_decode(w, v), "graph case eager")
