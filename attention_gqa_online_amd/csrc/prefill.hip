@@ -14,6 +14,9 @@
 //               consecutive 32-row blocks.
 //   K/V tiles of 64 keys are staged once in LDS and used by all 8 waves
 //   (every Q head of the group reads the same tile; the GQA reuse is explicit).
+//   Tiles go global -> LDS directly (no registers) into two buffers, so the
+//   next tile's loads run under the current tile's matrix work; one barrier
+//   per tile.
 //   Per wave and tile:
 //     S^T[64 keys x 32 rows] = K_tile . Q^T        (2 x D/2 MFMAs, A = K from LDS,
 //                                                 B = Q^T held in registers)
@@ -57,18 +60,63 @@ __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// 16-byte chunk index of a K/V element row inside an LDS tile row, XOR-
+// swizzled by the row so that the 32 lanes of an MFMA operand read (one row
+// each, same logical chunk) land in different LDS banks without padding.
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+    constexpr int SW = D / 4 < 16 ? D / 4 : 16;
+    return chunk ^ (row & (SW - 1));
+}
+
+// Copy one 64-row tile of K and of V for KV head g into LDS with direct
+// global->LDS loads (global_load_lds_dwordx4): each instruction moves 64
+// lanes x 16 bytes to consecutive LDS addresses; the lane picks which global
+// chunk fills its LDS slot, which is how the swizzle is applied. Rows past
+// m re-read row m - 1 (in bounds); the causal mask removes them.
+template <int D>
+__device__ __forceinline__ void load_tile_lds(const PrefillArgs &a, uint32_t g, uint32_t kt,
+                                              float *sk, float *sv, int wave, int lane) {
+    constexpr int CPR = D / 4;                    // 16-byte chunks per row
+    constexpr int NI = kBc * CPR / (kWaves * 64); // instructions per wave per tensor
+    static_assert(NI >= 1 && kBc * CPR % (kWaves * 64) == 0, "tile split over waves");
+    // opaque copy of the lane id: the per-lane source offsets below are then
+    // formed at each call instead of being hoisted out of the tile loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int l = (wave * NI + i) * 64 + ln;  // LDS chunk slot of this lane
+        const int row = l / CPR;
+        const int c = swz_chunk<D>(row, l % CPR);  // global chunk stored there
+        const uint32_t key = min(kt * kBc + row, a.m - 1);
+        const size_t goff = (size_t)key * a.kv_stride + (size_t)g * D + 4 * c;
+        const int loff = (wave * NI + i) * 64 * 4;  // floats; lane offset added by hardware
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(a.k + goff),
+            (__attribute__((address_space(3))) void *)(sk + loff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(a.v + goff),
+            (__attribute__((address_space(3))) void *)(sv + loff), 16, 0, 0);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
-    constexpr int KS = D + 4;   // LDS row stride (floats), padded against bank conflicts
     constexpr int NQ = D / 8;   // float4 chunks of the Q^T operand per lane
     constexpr int NMD = D / 32; // 32-row blocks of O^T (= floats per lane per V row)
-    constexpr int D4 = D / 4;
-    __shared__ float sK[kBc * KS];
-    __shared__ float sV[kBc * KS];
+    constexpr int NBUF = D <= 128 ? 2 : 1;  // double-buffered tiles when LDS allows
+    constexpr int TILE = kBc * D;           // floats per tile and tensor
+    __shared__ __attribute__((aligned(16))) float sK0[TILE];
+    __shared__ __attribute__((aligned(16))) float sV0[TILE];
+    __shared__ __attribute__((aligned(16))) float sK1[NBUF == 2 ? TILE : 4];
+    __shared__ __attribute__((aligned(16))) float sV1[NBUF == 2 ? TILE : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index in a scalar register: everything derived from it (pair,
+    // head, LDS load slots) stays out of the vector register file
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31;    // query column of this lane
     const int half = lane >> 5; // which of the two keys of a k-step
 
@@ -89,6 +137,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     const uint32_t my_kend = active ? min(qr0 + kBr, a.m) : 0;
     const uint32_t my_ntiles = (my_kend + kBc - 1) / kBc;
 
+    load_tile_lds<D>(a, g, 0, sK0, sV0, wave, lane);
+
     // Q^T operand: lane (j, half) holds Q[qi][8u + 4half + 0..3] for u < D/8
     float4 qt[NQ];
     {
@@ -105,89 +155,135 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 16; ++e) acc[md][e] = 0.f;
     float mrow = kNegInf, lrow = 0.f;
 
-    const float *kg = a.k + (size_t)g * D;
-    const float *vg = a.v + (size_t)g * D;
+    // matrix work of one tile (sk, sv in LDS) for this wave
+    auto tile = [&](const float *sk, const float *sv, uint32_t kt) {
+        if (kt < my_ntiles) {  // wave-uniform: not yet past this wave's diagonal
+            // this lane's swizzle key, made opaque per tile so the swizzled
+            // LDS addresses are formed where they are used instead of being
+            // hoisted out of the loop and held in registers
+            int xj = j;
+            asm volatile("" : "+v"(xj));
 
-    for (uint32_t kt = 0; kt < ntiles; ++kt) {
-        __syncthreads();  // previous tile fully consumed
-        for (int idx = tid; idx < kBc * D4; idx += kWaves * 64) {
-            const int row = idx / D4;
-            const int c4 = idx % D4;
-            const uint32_t key = kt * kBc + row;
-            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-            if (key < a.m) {
-                kx = ld4(kg + (size_t)key * a.kv_stride + 4 * c4);
-                vx = ld4(vg + (size_t)key * a.kv_stride + 4 * c4);
+            // S^T = K_tile . Q^T, two 32-key blocks
+            floatx16 s0, s1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) {
+                const int c = 2 * u + half;
+                const float *kp = sk + j * D + 4 * swz_chunk<D>(xj, c);
+                const float4 ka = ld4(kp);
+                const float4 kb = ld4(kp + 32 * D);  // row 32 + j has the same swizzle
+                s0 = mfma32(ka.x, qt[u].x, s0);
+                s1 = mfma32(kb.x, qt[u].x, s1);
+                s0 = mfma32(ka.y, qt[u].y, s0);
+                s1 = mfma32(kb.y, qt[u].y, s1);
+                s0 = mfma32(ka.z, qt[u].z, s0);
+                s1 = mfma32(kb.z, qt[u].z, s1);
+                s0 = mfma32(ka.w, qt[u].w, s0);
+                s1 = mfma32(kb.w, qt[u].w, s1);
             }
-            st4(&sK[row * KS + 4 * c4], kx);
-            st4(&sV[row * KS + 4 * c4], vx);
-        }
-        __syncthreads();
-        if (kt >= my_ntiles) continue;  // wave-uniform: beyond this wave's diagonal
 
-        // S^T = K_tile . Q^T, two 32-key blocks
-        floatx16 s0, s1;
+            // causal mask on tiles that reach past this wave's first row (also
+            // removes the re-read rows past m: their keys exceed every query)
+            if (kt * kBc + kBc - 1 > qr0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const float4 ka = *reinterpret_cast<const float4 *>(&sK[j * KS + 8 * u + 4 * half]);
-            const float4 kb = *reinterpret_cast<const float4 *>(&sK[(32 + j) * KS + 8 * u + 4 * half]);
-            s0 = mfma32(ka.x, qt[u].x, s0);
-            s1 = mfma32(kb.x, qt[u].x, s1);
-            s0 = mfma32(ka.y, qt[u].y, s0);
-            s1 = mfma32(kb.y, qt[u].y, s1);
-            s0 = mfma32(ka.z, qt[u].z, s0);
-            s1 = mfma32(kb.z, qt[u].z, s1);
-            s0 = mfma32(ka.w, qt[u].w, s0);
-            s1 = mfma32(kb.w, qt[u].w, s1);
-        }
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t key = kt * kBc + 8 * (e / 4) + 4 * half + (e % 4);
+                    if (key > qi) s0[e] = kNegInf;
+                    if (key + 32 > qi) s1[e] = kNegInf;
+                }
+            }
 
-        // causal mask on tiles that reach past this wave's first row
-        if (kt * kBc + kBc - 1 > qr0) {
+            // online softmax for query row qi (this lane and lane ^ 32 share it)
+            float mx = kNegInf;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(mrow, mx);
+            const float cf = fast_exp2(mrow - mnew);
+            mrow = mnew;
+            float ls = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const uint32_t key = kt * kBc + 8 * (e / 4) + 4 * half + (e % 4);
-                if (key > qi) s0[e] = kNegInf;
-                if (key + 32 > qi) s1[e] = kNegInf;
+                s0[e] = fast_exp2(s0[e] - mnew);
+                s1[e] = fast_exp2(s1[e] - mnew);
+                ls += s0[e] + s1[e];
+            }
+            lrow = lrow * cf + ls;
+#pragma unroll
+            for (int md = 0; md < NMD; ++md)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[md][e] *= cf;
+
+            // O^T += V_tile^T . P^T; k-step (block mb, register e) uses key
+            // 32mb + 8(e/4) + 4half + e%4, the key register e of S^T holds
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key0 = 8 * (e / 4) + 4 * half + (e % 4);
+                float va[NMD], vb[NMD];
+                if constexpr (NMD % 4 == 0) {
+                    // NMD consecutive floats = whole 16-byte chunks: ds_read_b128
+#pragma unroll
+                    for (int q4 = 0; q4 < NMD / 4; ++q4) {
+                        const int cchunk = NMD / 4 * xj + q4;
+                        const float *vp = sv + key0 * D + 4 * swz_chunk<D>(key0, cchunk);
+                        const float4 x = ld4(vp);
+                        const float4 y = ld4(vp + 32 * D);  // row 32 + key0: same swizzle
+                        va[4 * q4 + 0] = x.x; va[4 * q4 + 1] = x.y;
+                        va[4 * q4 + 2] = x.z; va[4 * q4 + 3] = x.w;
+                        vb[4 * q4 + 0] = y.x; vb[4 * q4 + 1] = y.y;
+                        vb[4 * q4 + 2] = y.z; vb[4 * q4 + 3] = y.w;
+                    }
+                } else if constexpr (NMD == 2) {
+                    // two consecutive floats, half a 16-byte chunk: ds_read_b64
+                    const int f = 2 * xj;
+                    const float *vp = sv + key0 * D + 4 * swz_chunk<D>(key0, f / 4) + f % 4;
+                    const float2 x = *reinterpret_cast<const float2 *>(vp);
+                    const float2 y = *reinterpret_cast<const float2 *>(vp + 32 * D);
+                    va[0] = x.x; va[1] = x.y;
+                    vb[0] = y.x; vb[1] = y.y;
+                } else {
+#pragma unroll
+                    for (int md = 0; md < NMD; ++md) {
+                        const int f = NMD * xj + md;  // float index in the V row
+                        const float *vp = sv + key0 * D + 4 * swz_chunk<D>(key0, f / 4) + f % 4;
+                        va[md] = vp[0];
+                        vb[md] = vp[32 * D];  // row 32 + key0 has the same swizzle
+                    }
+                }
+#pragma unroll
+                for (int md = 0; md < NMD; ++md) acc[md] = mfma32(va[md], s0[e], acc[md]);
+#pragma unroll
+                for (int md = 0; md < NMD; ++md) acc[md] = mfma32(vb[md], s1[e], acc[md]);
             }
         }
+    };
 
-        // online softmax for query row qi (this lane and lane ^ 32 share it)
-        float mx = kNegInf;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow, mx);
-        const float cf = fast_exp2(mrow - mnew);
-        mrow = mnew;
-        float ls = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s0[e] = fast_exp2(s0[e] - mnew);
-            s1[e] = fast_exp2(s1[e] - mnew);
-            ls += s0[e] + s1[e];
+    if constexpr (NBUF == 2) {
+        // two static buffers, tiles alternate between them: every LDS read
+        // and every direct load names its buffer, so the compiler can see
+        // the next tile's loads do not touch the tile being read
+        for (uint32_t kt = 0; kt < ntiles; kt += 2) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
+            __syncthreads();  // every wave's loads landed; buffer 1 is free
+            if (kt + 1 < ntiles) load_tile_lds<D>(a, g, kt + 1, sK1, sV1, wave, lane);
+            tile(sK0, sV0, kt);
+            if (kt + 1 >= ntiles) break;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();  // buffer 0 is free
+            if (kt + 2 < ntiles) load_tile_lds<D>(a, g, kt + 2, sK0, sV0, wave, lane);
+            tile(sK1, sV1, kt + 1);
         }
-        lrow = lrow * cf + ls;
-#pragma unroll
-        for (int md = 0; md < NMD; ++md)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[md][e] *= cf;
-
-        // O^T += V_tile^T . P^T; k-step (block mb, register e) uses key
-        // 32mb + 8(e/4) + 4half + e%4, the key register e of S^T holds
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key0 = 8 * (e / 4) + 4 * half + (e % 4);
-            const float *v0 = &sV[key0 * KS + NMD * j];
-            const float *v1 = &sV[(32 + key0) * KS + NMD * j];
-            float va[NMD], vb[NMD];
-#pragma unroll
-            for (int md = 0; md < NMD; ++md) { va[md] = v0[md]; vb[md] = v1[md]; }
-#pragma unroll
-            for (int md = 0; md < NMD; ++md) acc[md] = mfma32(va[md], s0[e], acc[md]);
-#pragma unroll
-            for (int md = 0; md < NMD; ++md) acc[md] = mfma32(vb[md], s1[e], acc[md]);
+    } else {
+        for (uint32_t kt = 0; kt < ntiles; ++kt) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            tile(sK0, sV0, kt);
+            if (kt + 1 < ntiles) {
+                __syncthreads();  // single buffer: everyone done before it is refilled
+                load_tile_lds<D>(a, g, kt + 1, sK0, sV0, wave, lane);
+            }
         }
     }
 
