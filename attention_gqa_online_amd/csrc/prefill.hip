@@ -11,7 +11,9 @@
 //   workgroup = 8 waves sharing one KV head g. Wave w of workgroup i owns the
 //               (row block, head) pair i*8 + w of the group, enumerated row
 //               block major, so the waves of a workgroup sit in at most a few
-//               consecutive 32-row blocks.
+//               consecutive 32-row blocks. Grids too small to fill the chip
+//               twice pair row blocks u and n-1-u instead (waves 0-3 / 4-7,
+//               four heads each), balancing the causal work per workgroup.
 //   K/V tiles of 64 keys are staged once in LDS and used by all 8 waves
 //   (every Q head of the group reads the same tile; the GQA reuse is explicit).
 //   Tiles go global -> LDS directly (no registers) into two buffers, so the
@@ -44,6 +46,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kBr = 32;  // query rows per wave
 constexpr int kBc = 64;  // keys per LDS tile
+constexpr int kCus = 256;  // compute units of an MI355X
 
 struct PrefillArgs {
     const float *q;
@@ -52,7 +55,10 @@ struct PrefillArgs {
     float *o;
     uint32_t m, q_stride, kv_stride, hpk, kv_heads;
     uint32_t n_pairs;      // hpk * ceil(m / 32)
-    uint32_t wg_per_group; // ceil(n_pairs / 8)
+    uint32_t wg_per_group; // workgroups per KV head
+    uint32_t n_rb;         // ceil(m / 32)
+    uint32_t zigzag;       // 1: waves 0-3 / 4-7 take row blocks u / n_rb-1-u
+    uint32_t nsub;         // zigzag: workgroups per row-block pair (ceil(hpk / 4))
     float qscale;          // (1/sqrt(d) in f32) * log2(e)
 };
 
@@ -122,17 +128,33 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 
     const uint32_t g = blockIdx.x % a.kv_heads;
     const uint32_t wi = a.wg_per_group - 1 - blockIdx.x / a.kv_heads;  // heavy first
-    const uint32_t pair = wi * kWaves + wave;
-    const bool active = pair < a.n_pairs;
-    const uint32_t rb = pair / a.hpk;
-    const uint32_t h = g * a.hpk + pair % a.hpk;
+    bool active;
+    uint32_t rb, hl, rb_last;  // this wave's row block and head; the workgroup's last block
+    if (a.zigzag) {
+        // small grids: waves 0-3 take heads of row block u, waves 4-7 the same
+        // heads of block n_rb-1-u, so each SIMD runs one short and one long
+        // wave and every workgroup has about the same work
+        const uint32_t u = wi / a.nsub;
+        hl = (wi % a.nsub) * 4 + (wave & 3);
+        const uint32_t lo = u, hi = a.n_rb - 1 - u;
+        rb = wave < 4 ? lo : hi;
+        active = hl < a.hpk && (wave < 4 || hi > lo);
+        rb_last = hi;
+    } else {
+        // row-block-major pairs: workgroup wi owns pairs wi*8 .. wi*8+7
+        const uint32_t pair = wi * kWaves + wave;
+        active = pair < a.n_pairs;
+        rb = pair / a.hpk;
+        hl = pair % a.hpk;
+        rb_last = min(wi * kWaves + kWaves - 1, a.n_pairs - 1) / a.hpk;
+    }
+    const uint32_t h = g * a.hpk + (active ? hl : 0);
     const uint32_t qr0 = rb * kBr;
     const uint32_t qi = qr0 + j;
     const bool qvalid = active && qi < a.m;
 
     // keys this workgroup needs: [0, kend)
-    const uint32_t last_pair = min(wi * kWaves + kWaves - 1, a.n_pairs - 1);
-    const uint32_t kend = min((last_pair / a.hpk) * kBr + kBr, a.m);
+    const uint32_t kend = min(rb_last * kBr + kBr, a.m);
     const uint32_t ntiles = (kend + kBc - 1) / kBc;
     const uint32_t my_kend = active ? min(qr0 + kBr, a.m) : 0;
     const uint32_t my_ntiles = (my_kend + kBc - 1) / kBc;
@@ -142,7 +164,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     // Q^T operand: lane (j, half) holds Q[qi][8u + 4half + 0..3] for u < D/8
     float4 qt[NQ];
     {
-        const float *qrow = a.q + (size_t)(qvalid ? qi : 0) * a.q_stride + (size_t)(active ? h : 0) * D;
+        const float *qrow = a.q + (size_t)(qvalid ? qi : 0) * a.q_stride + (size_t)h * D;
         const float qs = qvalid ? a.qscale : 0.f;
 #pragma unroll
         for (int u = 0; u < NQ; ++u) qt[u] = ld4(qrow + 8 * u + 4 * half) * qs;
@@ -324,8 +346,16 @@ hipError_t launch_prefill(const float *q, const float *k, const float *v, float 
     a.hpk = heads_per_kv;
     a.kv_heads = num_q_heads / heads_per_kv;
     const uint32_t n_rb = (m + kBr - 1) / kBr;
+    a.n_rb = n_rb;
     a.n_pairs = heads_per_kv * n_rb;
     a.wg_per_group = (a.n_pairs + kWaves - 1) / kWaves;
+    // a grid under two workgroups per CU is bound by its heaviest workgroup:
+    // pair short and long row blocks instead
+    a.nsub = (heads_per_kv + 3) / 4;
+    if ((uint64_t)a.wg_per_group * a.kv_heads < 2 * kCus) {
+        a.zigzag = 1;
+        a.wg_per_group = (n_rb + 1) / 2 * a.nsub;
+    }
     a.qscale = (1.0f / sqrtf((float)head_dim)) * kLog2e;
     const uint32_t grid = a.wg_per_group * a.kv_heads;
     switch (head_dim) {

@@ -326,6 +326,22 @@ def test_prefill_long_workload_sampled(dev):
     _assert_close(o[rows, heads], ref, _vmax_prefill(w, v), "long prefill sample")
 
 
+def test_prefill_row_block_major_path_ragged(dev):
+    """A grid of two or more workgroups per CU (here 1032) takes the
+    row-block-major work map; m = 4100 leaves a ragged last row block.
+    Sample: the last 40 rows of every head plus 1500 seeded random pairs."""
+    w = synth.PrefillWorkload("case", m=4100, num_q_heads=64, heads_per_kv=8, head_dim=128,
+                              q_stride=64 * 128, kv_stride=8 * 128, seed=4100)
+    q, k, v = synth.prefill_inputs(w)
+    o = _heads(w, _gpu_prefill(dev, w, q, k, v))
+    rng = np.random.default_rng(4101)
+    rows = [np.repeat(np.arange(w.m - 40, w.m), 64), rng.integers(0, w.m, 1500)]
+    heads = [np.tile(np.arange(64), 40), rng.integers(0, 64, 1500)]
+    rows, heads = np.concatenate(rows), np.concatenate(heads)
+    ref = _ref_prefill(w, q, k, v, rows=rows, heads=heads)
+    _assert_close(o[rows, heads], ref, _vmax_prefill(w, v), "row-block-major ragged")
+
+
 PREFILL_SWEEP = [
     # (m, hq, hpk, d)
     (1, 1, 1, 32), (2, 2, 1, 64), (15, 4, 2, 32), (16, 4, 2, 32), (17, 4, 2, 32),
