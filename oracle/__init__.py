@@ -64,6 +64,13 @@ def _bind(lib):
         ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
         ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t, _U32P, _U32P,
         _F64P]
+    lib.oracle_rope.restype = ctypes.c_int
+    lib.oracle_rope.argtypes = [_F32P, _F32P, _F32P, ctypes.c_size_t, ctypes.c_uint32, _F64P]
+    lib.oracle_decode_rope_append.restype = ctypes.c_int
+    lib.oracle_decode_rope_append.argtypes = [
+        _F32P, _F32P, _F32P, _F32P, _F32P, _F32P, _F32P, ctypes.c_uint32,
+        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_float, _F64P]
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [
         _F32P, _F32P, _F32P, _F32P, ctypes.c_uint32, ctypes.c_uint32,
@@ -174,6 +181,39 @@ class Oracle:
             raise ValueError("oracle_kv_append rejected its arguments")
 
 
+    def rope(self, x, cos_t, sin_t):
+        """Rotate-half rotary embedding of the rows of x ([..., d] float32)
+        with per-pair cos/sin ([d/2] float32); returns float64."""
+        d = x.shape[-1]
+        if cos_t.size < d // 2 or sin_t.size < d // 2:
+            raise ValueError("cos/sin need d/2 entries")
+        out = np.empty(x.shape, dtype=np.float64)
+        rc = self._lib.oracle_rope(_f32(np.ascontiguousarray(x), "x"), _f32(cos_t, "cos_t"),
+                                   _f32(sin_t, "sin_t"), x.size // d, d,
+                                   out.ctypes.data_as(_F64P))
+        if rc != 0:
+            raise ValueError("oracle_rope rejected its arguments")
+        return out
+
+    def decode_rope_append(self, q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache,
+                           batch, num_heads, kv_heads, head_dim, max_seq, position,
+                           window, scale):
+        """Fused decode step with rotary embedding; updates the caches in
+        place (rotated K, raw V at `position`) and returns [B, Hq, d] fp64."""
+        n_cache = batch * kv_heads * max_seq * head_dim
+        if k_cache.size < n_cache or v_cache.size < n_cache:
+            raise ValueError("cache arrays smaller than the stated shape")
+        out = np.empty((batch, num_heads, head_dim), dtype=np.float64)
+        rc = self._lib.oracle_decode_rope_append(
+            _f32(q_raw, "q_raw"), _f32(k_raw, "k_raw"), _f32(v_raw, "v_raw"),
+            _f32(cos_t, "cos_t"), _f32(sin_t, "sin_t"), _f32(k_cache, "k_cache", True),
+            _f32(v_cache, "v_cache", True), batch, num_heads, kv_heads, head_dim,
+            max_seq, position, window, ctypes.c_float(scale), out.ctypes.data_as(_F64P))
+        if rc != 0:
+            raise ValueError("oracle_decode_rope_append rejected its arguments")
+        return out
+
+
 _default = None
 
 
@@ -205,3 +245,11 @@ def decode(*args, **kw) -> np.ndarray:
 
 def kv_append(*args, **kw) -> None:
     return default().kv_append(*args, **kw)
+
+
+def rope(*args, **kw) -> np.ndarray:
+    return default().rope(*args, **kw)
+
+
+def decode_rope_append(*args, **kw) -> np.ndarray:
+    return default().decode_rope_append(*args, **kw)

@@ -32,6 +32,15 @@
  *    KV-append-both kernels):
  *    cache[b, g, position, :] = src[b, g, :] for K and V, nothing else written.
  *
+ *  - Rotary embedding and the fused decode step (glia honeycrisp
+ *    "attention.rs" page, fused RoPE + KV-append + decode kernel and its doc):
+ *    rotate-half pairs element i with element i + d/2 (i < d/2) and turns
+ *    each pair by the angle whose cosine and sine are cos[i], sin[i]:
+ *    y[i] = x[i] cos[i] - x[i+d/2] sin[i], y[i+d/2] = x[i] sin[i] + x[i+d/2] cos[i].
+ *    The step rotates the current token's q (every head) and new K row
+ *    (every KV head), writes the rotated K row and the raw V row into the
+ *    caches at `position`, then decodes with total_seq = position + 1.
+ *
  * Each softmax is materialised and taken in two passes over the stored
  * scores of one query row: first the maximum, then the exponentials and
  * their sum; the output is the sum of V rows weighted by e_j / Z. All
@@ -220,4 +229,130 @@ int oracle_kv_append(const float *k_src, const float *v_src, float *k_cache,
             }
         }
     return 0;
+}
+
+/* Rotate-half rotary embedding of one vector of d elements (d even), in fp64
+ * on the fp32 input; out may not alias x. */
+static void rope(const float *x, const float *cs, const float *sn, uint32_t d,
+                 double *out)
+{
+    uint32_t half = d / 2;
+    for (uint32_t i = 0; i < half; ++i) {
+        double a = x[i], b = x[i + half], c = cs[i], s = sn[i];
+        out[i] = a * c - b * s;
+        out[i + half] = a * s + b * c;
+    }
+}
+
+/* Rotary embedding of n vectors of d elements: x [n, d] -> out [n, d] fp64. */
+int oracle_rope(const float *x, const float *cos_t, const float *sin_t,
+                size_t n, uint32_t d, double *out)
+{
+    if (d == 0 || d % 2)
+        return -1;
+    for (size_t r = 0; r < n; ++r)
+        rope(x + r * d, cos_t, sin_t, d, out + r * d);
+    return 0;
+}
+
+/*
+ * One fused decode step with rotary embedding: rotate q (all heads) and the
+ * new K rows, write rotated K and raw V at `position`, decode over
+ * [w0, position]. The caches are updated in place with the rotated K rows
+ * rounded to fp32 (what a cache of fp32 holds); the scores of the new row use
+ * the fp64 rotation of q and k. out: [batch, num_heads, head_dim] doubles.
+ */
+int oracle_decode_rope_append(const float *q_raw, const float *k_raw,
+                              const float *v_raw, const float *cos_t,
+                              const float *sin_t, float *k_cache,
+                              float *v_cache, uint32_t batch,
+                              uint32_t num_heads, uint32_t kv_heads,
+                              uint32_t head_dim, uint32_t max_seq,
+                              uint32_t position, uint32_t window, float scale,
+                              double *out)
+{
+    if (kv_heads == 0 || head_dim == 0 || head_dim % 2 ||
+        num_heads % kv_heads || position >= max_seq)
+        return -1;
+    uint32_t repeat = num_heads / kv_heads;
+    uint32_t total_seq = position + 1;
+    uint32_t window_start =
+        (window > 0 && total_seq > window) ? total_seq - window : 0;
+    size_t n = (size_t)(total_seq - window_start);
+    size_t d = head_dim;
+    double *qr = (double *)malloc(sizeof(double) * d * num_heads * batch);
+    double *kr = (double *)malloc(sizeof(double) * d * kv_heads * batch);
+    if (!qr || !kr) {
+        free(qr);
+        free(kr);
+        return -1;
+    }
+    oracle_rope(q_raw, cos_t, sin_t, (size_t)batch * num_heads, head_dim, qr);
+    oracle_rope(k_raw, cos_t, sin_t, (size_t)batch * kv_heads, head_dim, kr);
+    /* the append: rotated K (as fp32) and raw V at `position` */
+    for (uint32_t b = 0; b < batch; ++b)
+        for (uint32_t g = 0; g < kv_heads; ++g) {
+            size_t src = ((size_t)b * kv_heads + g) * d;
+            size_t dst = (((size_t)b * kv_heads + g) * max_seq + position) * d;
+            for (size_t e = 0; e < d; ++e) {
+                k_cache[dst + e] = (float)kr[src + e];
+                v_cache[dst + e] = v_raw[src + e];
+            }
+        }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *scores = (double *)malloc(sizeof(double) * n);
+        if (!scores) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (size_t t = 0; t < (size_t)batch * num_heads; ++t) {
+            if (!scores)
+                continue;
+            uint32_t b = (uint32_t)(t / num_heads), h = (uint32_t)(t % num_heads);
+            uint32_t g = h / repeat;
+            const double *qh = qr + t * d;
+            size_t base = (((size_t)b * kv_heads + g) * max_seq + window_start) * d;
+            const float *k0 = k_cache + base, *v0 = v_cache + base;
+            size_t j, e;
+            /* scores: cached rows as stored; the new row from the fp64 rotation */
+            for (j = 0; j < n; ++j) {
+                double dot = 0.0;
+                if (window_start + j == position) {
+                    const double *kn = kr + ((size_t)b * kv_heads + g) * d;
+                    for (e = 0; e < d; ++e)
+                        dot += qh[e] * kn[e];
+                } else {
+                    const float *kj = k0 + j * d;
+                    for (e = 0; e < d; ++e)
+                        dot += qh[e] * (double)kj[e];
+                }
+                scores[j] = (double)scale * dot;
+            }
+            double mu = -INFINITY;
+            for (j = 0; j < n; ++j)
+                if (scores[j] > mu)
+                    mu = scores[j];
+            double z = 0.0;
+            for (j = 0; j < n; ++j) {
+                scores[j] = exp(scores[j] - mu);
+                z += scores[j];
+            }
+            double *o = out + t * d;
+            for (e = 0; e < d; ++e)
+                o[e] = 0.0;
+            for (j = 0; j < n; ++j) {
+                const float *vj = v0 + j * d;
+                double w = scores[j] / z;
+                for (e = 0; e < d; ++e)
+                    o[e] += w * (double)vj[e];
+            }
+        }
+        free(scores);
+    }
+    free(qr);
+    free(kr);
+    return bad ? -1 : 0;
 }

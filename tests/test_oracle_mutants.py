@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_rope as rope_pins
 
 MUTANTS = {
     "gqa_interleaved_prefill": ("uint32_t g = h / heads_per_kv;",
@@ -46,6 +47,9 @@ MUTANTS = {
                          "+ position + 1 - (position + 1 == max_seq))\n                         * head_dim;"),
     "append_v_from_k": ("v_cache[dst + e] = v_src[src + e];",
                         "v_cache[dst + e] = k_src[src + e];"),
+    "rope_sign": ("out[i] = a * c - b * s;", "out[i] = a * c + b * s;"),
+    "rope_pair_index": ("double a = x[i], b = x[i + half]", "double a = x[i], b = x[half - 1 - i]"),
+    "rope_step_raw_k": ("dot += qh[e] * kn[e];", "dot += qh[e] * (double)k_raw[((size_t)b * kv_heads + g) * d + e];"),
 }
 
 PIN_CALLS = [
@@ -67,6 +71,11 @@ PIN_CALLS = [
     ("sdpa_prefill", lambda o, g: pins.test_prefill_matches_torch_sdpa_fp64(o, 33, 6, 3, 64, 32, 64)),
     ("sdpa_decode", lambda o, g: pins.test_decode_matches_torch_sdpa_fp64(o, 1, 8, 2, 64, 20, 11, 3)),
     ("kv_append", lambda o, g: pins.test_kv_append_writes_only_position(o)),
+    ("rope_complex", lambda o, g: rope_pins.test_rope_is_complex_rotation(o)),
+    ("rope_special", lambda o, g: rope_pins.test_rope_special_angles(o)),
+    ("rope_norms", lambda o, g: rope_pins.test_rope_preserves_pair_norms_and_composes(o)),
+    ("rope_relative", lambda o, g: rope_pins.test_rope_relative_position(o)),
+    ("rope_step", lambda o, g: rope_pins.test_decode_rope_append_is_rotate_append_decode(o)),
 ]
 
 
