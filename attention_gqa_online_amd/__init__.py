@@ -20,6 +20,10 @@ import still succeeds, but the first call raises.
                        num_heads, kv_heads, head_dim, max_seq, position,
                        window, scale, workspace, workspace_bytes=None,
                        stream=None)
+    attn_decode_rope_append(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache,
+                            v_cache, out, batch, num_heads, kv_heads,
+                            head_dim, max_seq, position, window, scale,
+                            workspace, workspace_bytes=None, stream=None)
     attn_status_string(status) -> str
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed, and
@@ -35,7 +39,8 @@ __all__ = [
     "AttnError", "ATTN_OK", "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED",
     "ATTN_ERR_HIP", "SO_PATH", "library", "attn_prefill_causal",
     "attn_decode_workspace_bytes", "attn_decode", "kv_append",
-    "attn_decode_append", "attn_status_string", "decode_workspace",
+    "attn_decode_append", "attn_decode_rope_append", "attn_status_string",
+    "decode_workspace",
 ]
 
 SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -43,7 +48,8 @@ SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 
 EXPORTS = ("attn_prefill_causal", "attn_decode_workspace_bytes", "attn_decode",
-           "kv_append", "attn_decode_append", "attn_status_string")
+           "kv_append", "attn_decode_append", "attn_decode_rope_append",
+           "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -82,6 +88,9 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32,
                                            _u32, _u32, _u32, _u32, ctypes.c_float, _vp,
                                            ctypes.c_size_t, _vp]
+        lib.attn_decode_rope_append.restype = ctypes.c_int
+        lib.attn_decode_rope_append.argtypes = [_vp] * 8 + [_u32] * 7 + [
+            ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ctypes.c_int]
         _lib = lib
@@ -186,6 +195,17 @@ def kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads, head_dim,
     _check("kv_append", st)
 
 
+def _workspace_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return workspace_bytes
+    import torch
+    if workspace is None:
+        return 0
+    if isinstance(workspace, torch.Tensor):
+        return workspace.numel() * workspace.element_size()
+    raise ValueError("workspace_bytes is required for an int workspace")
+
+
 def attn_decode_append(q, k_new, v_new, k_cache, v_cache, out, batch, num_heads,
                        kv_heads, head_dim, max_seq, position, window, scale,
                        workspace, workspace_bytes=None, stream=None) -> None:
@@ -193,14 +213,7 @@ def attn_decode_append(q, k_new, v_new, k_cache, v_cache, out, batch, num_heads,
     ``[w0, position]`` (one decode step)."""
     n_src = batch * kv_heads * head_dim
     n_cache = batch * kv_heads * max_seq * head_dim
-    if workspace_bytes is None:
-        import torch
-        if workspace is None:
-            workspace_bytes = 0
-        elif isinstance(workspace, torch.Tensor):
-            workspace_bytes = workspace.numel() * workspace.element_size()
-        else:
-            raise ValueError("workspace_bytes is required for an int workspace")
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
     st = library().attn_decode_append(
         _ptr(q, "q", batch * num_heads * head_dim), _ptr(k_new, "k_new", n_src),
         _ptr(v_new, "v_new", n_src), _ptr(k_cache, "k_cache", n_cache),
@@ -208,3 +221,23 @@ def attn_decode_append(q, k_new, v_new, k_cache, v_cache, out, batch, num_heads,
         batch, num_heads, kv_heads, head_dim, max_seq, position, window, float(scale),
         _ptr(workspace, "workspace"), int(workspace_bytes), _stream(stream))
     _check("attn_decode_append", st)
+
+
+def attn_decode_rope_append(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache,
+                            out, batch, num_heads, kv_heads, head_dim, max_seq,
+                            position, window, scale, workspace,
+                            workspace_bytes=None, stream=None) -> None:
+    """One decode step with rotate-half rotary embedding: rotate q and the
+    new K rows by ``cos_t``/``sin_t`` (``[head_dim/2]``, the angles at
+    ``position``), append rotated K and raw V at ``position``, and decode."""
+    n_src = batch * kv_heads * head_dim
+    n_cache = batch * kv_heads * max_seq * head_dim
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    st = library().attn_decode_rope_append(
+        _ptr(q_raw, "q_raw", batch * num_heads * head_dim), _ptr(k_raw, "k_raw", n_src),
+        _ptr(v_raw, "v_raw", n_src), _ptr(cos_t, "cos_t", head_dim // 2),
+        _ptr(sin_t, "sin_t", head_dim // 2), _ptr(k_cache, "k_cache", n_cache),
+        _ptr(v_cache, "v_cache", n_cache), _ptr(out, "out", batch * num_heads * head_dim),
+        batch, num_heads, kv_heads, head_dim, max_seq, position, window, float(scale),
+        _ptr(workspace, "workspace"), int(workspace_bytes), _stream(stream))
+    _check("attn_decode_rope_append", st)

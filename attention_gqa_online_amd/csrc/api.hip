@@ -82,12 +82,52 @@ attn_status attn_decode(const float *q, const float *k_cache, const float *v_cac
                                         nullptr, stream));
 }
 
+namespace {
+
+attn_status decode_step(const float *q, const float *k_new, const float *v_new,
+                        const float *cos_t, const float *sin_t, float *k_cache,
+                        float *v_cache, float *out, uint32_t batch, uint32_t num_heads,
+                        uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                        uint32_t position, uint32_t window, float scale, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+}  // namespace
+
 attn_status attn_decode_append(const float *q, const float *k_new, const float *v_new,
                                float *k_cache, float *v_cache, float *out, uint32_t batch,
                                uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
                                uint32_t max_seq, uint32_t position, uint32_t window,
                                float scale, void *workspace, size_t workspace_bytes,
                                hipStream_t stream) {
+    return decode_step(q, k_new, v_new, nullptr, nullptr, k_cache, v_cache, out, batch,
+                       num_heads, kv_heads, head_dim, max_seq, position, window, scale,
+                       workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_rope_append(const float *q_raw, const float *k_raw,
+                                    const float *v_raw, const float *cos_t,
+                                    const float *sin_t, float *k_cache, float *v_cache,
+                                    float *out, uint32_t batch, uint32_t num_heads,
+                                    uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                                    uint32_t position, uint32_t window, float scale,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (batch != 0 && (!aligned16(cos_t) || !aligned16(sin_t))) return ATTN_ERR_INVALID;
+    return decode_step(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache, out, batch,
+                       num_heads, kv_heads, head_dim, max_seq, position, window, scale,
+                       workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+attn_status decode_step(const float *q, const float *k_new, const float *v_new,
+                        const float *cos_t, const float *sin_t, float *k_cache,
+                        float *v_cache, float *out, uint32_t batch, uint32_t num_heads,
+                        uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                        uint32_t position, uint32_t window, float scale, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
     if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
     if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
     if (position >= max_seq) return ATTN_ERR_INVALID;
@@ -97,14 +137,15 @@ attn_status attn_decode_append(const float *q, const float *k_new, const float *
     if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
         return ATTN_ERR_INVALID;
+    if (num_heads == 0) {  // nothing to attend: the append alone
+        return from_hip(attn::launch_kv_append(k_new, v_new, k_cache, v_cache, batch, kv_heads,
+                                               head_dim, max_seq, position, stream, cos_t,
+                                               sin_t));
+    }
     const uint32_t total_seq = position + 1;
     const attn::DecodePlan plan =
         attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window, true);
-    attn::DecodeAppend app{k_new, v_new, k_cache, v_cache};
-    if (num_heads == 0) {  // nothing to attend: the append alone
-        return from_hip(attn::launch_kv_append(k_new, v_new, k_cache, v_cache, batch, kv_heads,
-                                               head_dim, max_seq, position, stream));
-    }
+    attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, cos_t, sin_t};
     if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
     if (plan.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes))
         return ATTN_ERR_INVALID;
@@ -113,6 +154,10 @@ attn_status attn_decode_append(const float *q, const float *k_new, const float *
                                         head_dim, max_seq, total_seq, scale, workspace, &app,
                                         stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 attn_status kv_append(const float *k_src, const float *v_src, float *k_cache, float *v_cache,
                       uint32_t batch, uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,

@@ -92,4 +92,16 @@ __device__ __forceinline__ float4 ld4_stream(const float *p) {
     return make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Rotate-half rotary embedding (a rotation by angle theta_i of the pair
+// (x_i, x_{i+d/2}), i < d/2) of one element x whose pair partner is xp, or of
+// four componentwise: a first-half element becomes x c - xp s, a second-half
+// element xp s + x c, with c, s the cosine and sine of its pair's angle.
+__device__ __forceinline__ float rope_half1(float x, float xp, float c, float s, bool lo) {
+    return lo ? x * c - xp * s : xp * s + x * c;
+}
+__device__ __forceinline__ float4 rope_half(float4 x, float4 xp, float4 c, float4 s, bool lo) {
+    return make_float4(rope_half1(x.x, xp.x, c.x, s.x, lo), rope_half1(x.y, xp.y, c.y, s.y, lo),
+                       rope_half1(x.z, xp.z, c.z, s.z, lo), rope_half1(x.w, xp.w, c.w, s.w, lo));
+}
+
 }  // namespace attn

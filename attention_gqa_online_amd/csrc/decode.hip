@@ -60,6 +60,7 @@ inline uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1)
 DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
                        uint32_t head_dim, uint32_t total_seq, uint32_t window, bool append) {
     DecodePlan p{};
+    if (kv_heads == 0 || num_heads < kv_heads) return p;  // no head: no work, no workspace
     const uint32_t hpk = num_heads / kv_heads;
     p.n_chunks = ceil_div(hpk, 8);
     p.head_chunk = ceil_div(hpk, p.n_chunks);
@@ -116,6 +117,8 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
         a.k_dst = append->k_cache;
         a.v_dst = append->v_cache;
         a.position = total_seq - 1;
+        a.cos_t = append->cos_t;
+        a.sin_t = append->sin_t;
     }
     const uint32_t hc = plan.head_chunk, u = plan.units, ns = plan.n_split;
     switch (head_dim) {

@@ -54,6 +54,10 @@ struct DecodeArgs {
     float *k_dst;     // the caches, written at row `position`
     float *v_dst;
     uint32_t position;
+    // rotary embedding of the current token (rotate-half), or null:
+    // cos/sin [D/2] for `position`, applied to q and to the new K rows
+    const float *cos_t;
+    const float *sin_t;
     uint32_t num_heads, kv_heads, hpk, n_chunks, max_seq;
     uint32_t w0, total_seq, n_split, rows_per_split;
     float qscale;     // scale * log2(e): scores come out in log2 units
@@ -141,7 +145,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             const float *qh = a.q + ((size_t)b * a.num_heads + h0 + hq) * D + 4 * c;
             const float qs = hh < nh ? a.qscale : 0.f;
 #pragma unroll
-            for (int t = 0; t < NF4; ++t) qv[hh][t] = ld4(qh + 4 * LPR * t) * qs;
+            for (int t = 0; t < NF4; ++t) qv[hh][t] = ld4(qh + 4 * LPR * t);
+            if (a.cos_t != nullptr) {
+                // rotate-half rotary embedding of this head's q: element d0
+                // pairs with d0 +- D/2 and turns by cos/sin[d0 mod D/2]
+#pragma unroll
+                for (int t = 0; t < NF4; ++t) {
+                    const int d0 = 4 * (c + LPR * t);
+                    const bool lo = d0 < D / 2;
+                    const float4 xp = ld4(qh + 4 * LPR * t + (lo ? D / 2 : -D / 2));
+                    const float4 cc = ld4(a.cos_t + (d0 % (D / 2)));
+                    const float4 ss = ld4(a.sin_t + (d0 % (D / 2)));
+                    qv[hh][t] = rope_half(qv[hh][t], xp, cc, ss, lo);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NF4; ++t) qv[hh][t] = qv[hh][t] * qs;
         }
 
         // one row step: scores of `row` from kf, softmax weights, V accumulate.
@@ -328,9 +347,19 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 
     float M = kNegInf, num = 0.f, den = 0.f;
     if (a.k_new != nullptr) {
-        const float kn = a.k_new[(size_t)bg * D + tid];
+        const float *knp = a.k_new + (size_t)bg * D;
+        const float *qp = a.q + ((size_t)b * a.num_heads + h) * D;
+        float kn = knp[tid];
+        float qd = qp[tid];
         const float vn = a.v_new[(size_t)bg * D + tid];
-        const float qd = a.q[((size_t)b * a.num_heads + h) * D + tid] * a.qscale;
+        if (a.cos_t != nullptr) {  // rotate the new K row and q (rotate-half)
+            const bool lo = tid < D / 2;
+            const int partner = lo ? tid + D / 2 : tid - D / 2;
+            const float cc = a.cos_t[tid % (D / 2)], ss = a.sin_t[tid % (D / 2)];
+            kn = rope_half1(kn, knp[partner], cc, ss, lo);
+            qd = rope_half1(qd, qp[partner], cc, ss, lo);
+        }
+        qd *= a.qscale;
         M = block_sum<D>(qd * kn);  // the new row's score, log2 units
         num = vn;
         den = 1.f;

@@ -29,12 +29,15 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
                        uint32_t head_dim, uint32_t total_seq, uint32_t window,
                        bool append = false);
 
-// New K/V rows for attn_decode_append: written at `position` = total_seq - 1.
+// New K/V rows for attn_decode_append: written at `position` = total_seq - 1;
+// with cos/sin ([D/2] for that position) q and the new K rows are rotated.
 struct DecodeAppend {
     const float *k_new;
     const float *v_new;
     float *k_cache;
     float *v_cache;
+    const float *cos_t = nullptr;
+    const float *sin_t = nullptr;
 };
 
 hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
@@ -50,9 +53,11 @@ hipError_t launch_prefill(const float *q, const float *k, const float *v, float 
                           uint32_t head_dim, hipStream_t stream);
 
 // ---------------------------------------------------------------- append
+// With cos_t/sin_t ([head_dim/2]) the K rows are rotated (rotate-half) first.
 hipError_t launch_kv_append(const float *k_src, const float *v_src, float *k_cache,
                             float *v_cache, uint32_t batch, uint32_t kv_heads,
                             uint32_t head_dim, uint32_t max_seq, uint32_t position,
-                            hipStream_t stream);
+                            hipStream_t stream, const float *cos_t = nullptr,
+                            const float *sin_t = nullptr);
 
 }  // namespace attn

@@ -190,7 +190,22 @@ def bench_headline(args, dev):
     two["graph_replay_us_per_step"] = round(gwall * 1e3, 2)
     two["graph_replay_event_us_per_step"] = round(gev * 1e3, 2)
     log(f"[bench] graph replay: {gwall * 1e3:.1f} us/step wall, {gev * 1e3:.1f} us by events")
-    return w, value, ms_per_step, roof, host_set0, two
+    # the same step with rotary embedding (attn_decode_rope_append)
+    cs = [torch.from_numpy(x).to(dev) for x in synth.rope_tables(w.head_dim, pos)]
+    cp, sp = cs[0].data_ptr(), cs[1].data_ptr()
+
+    def rope_step(i):
+        qp, kp, vp, ksp, vsp = ptrs[i % 3]
+        A.attn_decode_rope_append(qp, ksp, vsp, cp, sp, kp, vp, outp, w.batch, w.num_heads,
+                                  w.kv_heads, w.head_dim, w.max_seq, pos, w.window, w.scale,
+                                  wsp, wsb, stream=sint)
+
+    ms3, wall3 = time_calls(rope_step, args.steps, args.warmup, stream)
+    rope = {"step": "attn_decode_rope_append", "median_us": round(statistics.median(ms3) * 1e3, 2),
+            "wall_us_per_step": round(wall3 * 1e3, 2),
+            "GB/s": round(bytes_ / (statistics.median(ms3) * 1e-3) / 1e9, 1)}
+    log(f"[bench] rotary decode step: median {rope['median_us']:.1f} us")
+    return w, value, ms_per_step, roof, host_set0, two, rope
 
 
 def cpu_baseline(w, host_set):
@@ -309,8 +324,8 @@ def main():
     dev = torch.device("cuda:0")
     modes = set(args.modes.split(","))
 
-    w, value, ms_per_step, roof, host_set, two = bench_headline(args, dev)
-    extra = {"decode_step_two_calls": two}
+    w, value, ms_per_step, roof, host_set, two, rope = bench_headline(args, dev)
+    extra = {"decode_step_two_calls": two, "decode_step_rope": rope}
     if "decode_window" in modes:
         extra["decode_window"] = bench_decode_window(args, dev)
     if "prefill_long" in modes:

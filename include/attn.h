@@ -11,6 +11,9 @@
  *   kv_append             write one new K row and V row per (sequence, KV head)
  *                         into the caches
  *   attn_decode_append    kv_append + attn_decode of the same token, two launches
+ *   attn_decode_rope_append
+ *                         the same decode step with rotary position embedding
+ *                         applied to q and to the new K rows on the way in
  *
  * Common rules
  *   - Every tensor is fp32, row-major. Every pointer is a DEVICE pointer owned
@@ -161,6 +164,47 @@ attn_status attn_decode_append(const float *q, const float *k_new, const float *
                                uint32_t head_dim, uint32_t max_seq, uint32_t position,
                                uint32_t window, float scale, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step with rotary position embedding (glia honeycrisp
+ * "attention.rs" page, the fused RoPE + KV-append + flash-decode kernel's
+ * doc): rotate the current token's raw q and K rows, append the rotated K row
+ * and the raw V row at `position`, then attend over [w0, position] as in
+ * attn_decode_append. The pages run one sequence and head_dim 128; here any
+ * batch and every built head_dim, one cos/sin table shared by the batch (all
+ * sequences decode the same position).
+ *
+ *   q_raw             [batch, num_heads, head_dim]  before rotation
+ *   k_raw, v_raw      [batch, kv_heads, head_dim]   the current token's rows,
+ *                                                   K before rotation
+ *   cos_t, sin_t      [head_dim / 2]   cos and sin of pair i's angle at
+ *                                      `position` (the caller's frequency
+ *                                      table; not range-checked)
+ *   k_cache, v_cache  [batch, kv_heads, max_seq, head_dim]
+ *   out               [batch, num_heads, head_dim]
+ *
+ * Rotation (rotate-half): element i < head_dim/2 pairs with i + head_dim/2;
+ *   x'[i]              = x[i] cos_t[i] - x[i + head_dim/2] sin_t[i]
+ *   x'[i + head_dim/2] = x[i] sin_t[i] + x[i + head_dim/2] cos_t[i]
+ * applied to every q_raw head and every k_raw row. Then
+ *   k_cache[b, g, position, :] = k'[b, g, :],  v_cache[b, g, position, :] = v_raw[b, g, :]
+ * and out is the attention of q' over cache rows [w0, position], the new
+ * row scored from k' in registers. Cache rows other than `position` are only
+ * read and must already hold rotated keys.
+ *
+ * workspace, errors and zero-work cases: as attn_decode_append; cos_t and
+ * sin_t must also be non-null and 16-byte aligned (ATTN_ERR_INVALID).
+ * num_heads == 0 only appends (the K rows still rotated).
+ */
+attn_status attn_decode_rope_append(const float *q_raw, const float *k_raw,
+                                    const float *v_raw, const float *cos_t,
+                                    const float *sin_t, float *k_cache,
+                                    float *v_cache, float *out, uint32_t batch,
+                                    uint32_t num_heads, uint32_t kv_heads,
+                                    uint32_t head_dim, uint32_t max_seq,
+                                    uint32_t position, uint32_t window,
+                                    float scale, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * KV-cache append of K and V in one launch (glia honeycrisp "attention.rs"

@@ -183,6 +183,15 @@ def append_inputs(batch: int, kv_heads: int, head_dim: int, seed: int,
     return k, v
 
 
+def rope_tables(head_dim: int, position: int, base: float = 10000.0):
+    """cos/sin tables ``[head_dim/2]`` float32 for one position: pair i turns
+    by position * base^(-2i/head_dim) (the usual geometric frequency
+    schedule; the fused rotary decode takes the tables as given inputs)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    theta = position * base ** (-2.0 * i / head_dim)
+    return np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # On-device generation for timing runs (large caches in milliseconds). Same
 # distributions and layouts as above, drawn with torch's seeded generator on

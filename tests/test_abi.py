@@ -174,3 +174,27 @@ def test_decode_append_argument_rules(lib):
     assert _decode_append(lib, ws_bytes=need // 4) == INVALID
     assert _decode_append(lib, ws=0) == INVALID
     assert _decode_append(lib, b=0) == OK                        # no work, no launch
+
+
+def _decode_rope(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, pos=63, window=0,
+                 scale=0.088, ws=P, ws_bytes=1 << 30, ptrs=(P,) * 8):
+    return lib.attn_decode_rope_append(*ptrs, b, hq, hkv, d, max_seq, pos, window,
+                                       ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+def test_decode_rope_append_argument_rules(lib):
+    assert _decode_rope(lib, d=48) == INVALID
+    assert _decode_rope(lib, d=192) == UNSUPPORTED
+    assert _decode_rope(lib, hkv=0) == INVALID
+    assert _decode_rope(lib, hq=12, hkv=5) == INVALID
+    assert _decode_rope(lib, pos=64, max_seq=64) == INVALID
+    assert _decode_rope(lib, scale=float("inf")) == INVALID
+    for i in range(8):   # every pointer: null, then misaligned
+        for bad in (0, P + 4):
+            ptrs = tuple(bad if j == i else P for j in range(8))
+            assert _decode_rope(lib, ptrs=ptrs) == INVALID, (i, bad)
+    need = lib.attn_decode_workspace_bytes(2, 12, 2, 128, 64, 0)
+    assert _decode_rope(lib, ws_bytes=need - 4) == INVALID
+    assert _decode_rope(lib, ws=0) == INVALID
+    assert _decode_rope(lib, b=0) == OK                            # no work, no launch
+    assert _decode_rope(lib, b=0, ptrs=(0,) * 8) == OK

@@ -225,6 +225,20 @@ def test_decode_append_matches_append_then_decode(dev, case):
     _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), str(case))
 
 
+def test_decode_append_no_heads_only_appends(dev):
+    """num_heads == 0: the step reduces to kv_append (bit-exact)."""
+    b, hkv, d, ms, pos = 2, 3, 128, 12, 5
+    ks, vs = synth.append_inputs(b, hkv, d, seed=31)
+    kc = torch.full((b, hkv, ms, d), 2.0, device=dev)
+    vc = torch.full((b, hkv, ms, d), -3.0, device=dev)
+    A.attn_decode_append(0, torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev), kc, vc,
+                         0, b, 0, hkv, d, ms, pos, 0, 0.1, None)
+    torch.cuda.synchronize()
+    kr, vr = np.full((b, hkv, ms, d), 2.0, np.float32), np.full((b, hkv, ms, d), -3.0, np.float32)
+    oracle.kv_append(ks, vs, kr, vr, b, hkv, d, ms, pos)
+    assert np.array_equal(kc.cpu().numpy(), kr) and np.array_equal(vc.cpu().numpy(), vr)
+
+
 def test_decode_append_full_decode_workload(dev):
     """The decode workload's shape (32 x 12 heads, 4096 positions) as a decode
     step: append at position 4095, attend all 4096 rows."""
@@ -233,6 +247,121 @@ def test_decode_append_full_decode_workload(dev):
     w, (q, k, v), got, kc, vc = _decode_append_case(dev, case, seed=w0.seed)
     assert np.array_equal(kc, k) and np.array_equal(vc, v)
     _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), "decode step")
+
+
+# --------------------------------------------------- decode step with RoPE
+
+def _rope_row_bound(x):
+    """Per-element bound for a rotated fp32 row against the fp64 rotation
+    rounded to fp32: each output is x c - x' s (or x' s + x c) with |c|,|s| <= 1;
+    a product rounding, the sum's rounding and the final cast each cost at
+    most 2^-24 of |x| + |x'|, so 3 * 2^-24 * (|x| + |x'|) < 2^-22 (|x| + |x'|)."""
+    d = x.shape[-1]
+    h = d // 2
+    partner = np.concatenate([x[..., h:], x[..., :h]], axis=-1)
+    return 2.0 ** -22 * (np.abs(x).astype(np.float64) + np.abs(partner))
+
+
+def _decode_rope_case(dev, case, seed, scale_angles=1.0):
+    b, hq, hkv, d, ms, pos, win = case
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, pos + 1, window=win, seed=seed)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=seed + 1)
+    cos_t, sin_t = synth.rope_tables(d, pos * scale_angles)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    out = torch.full((b, hq, d), float("nan"), device=dev)
+    ws = torch.full((max(1, A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win)),),
+                    0xFF, dtype=torch.uint8, device=dev)
+    A.attn_decode_rope_append(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
+                              torch.from_numpy(vn).to(dev), torch.from_numpy(cos_t).to(dev),
+                              torch.from_numpy(sin_t).to(dev), kd, vd, out, b, hq, hkv, d, ms,
+                              pos, win, w.scale, ws)
+    torch.cuda.synchronize()
+    ref = oracle.decode_rope_append(q, kn, vn, cos_t, sin_t, k, v, b, hq, hkv, d, ms, pos,
+                                    win, w.scale)   # updates k, v like the step
+    return w, (q, k, v, kn), ref, out.cpu().numpy(), kd.cpu().numpy(), vd.cpu().numpy()
+
+
+def _check_rope_step(w, pos, q, k, v, kn, ref, got, kc, vc, label):
+    # every cache row but `position` untouched, V row copied exactly
+    keep = np.ones(w.max_seq, dtype=bool)
+    keep[pos] = False
+    assert np.array_equal(kc[:, :, keep], k[:, :, keep]), label
+    assert np.array_equal(vc, v), label
+    # the rotated K row within the rounding bound of the fp64 rotation
+    err = np.abs(kc[:, :, pos].astype(np.float64) - k[:, :, pos])
+    assert np.all(err <= _rope_row_bound(kn)), (label, float(err.max()))
+    _assert_close(got, ref, _vmax_decode(w, v), label)
+
+
+@pytest.mark.parametrize("case", DECODE_APPEND_CASES,
+                         ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_pos{}_w{}".format(*c))
+def test_decode_rope_append_matches_oracle(dev, case):
+    w, (q, k, v, kn), ref, got, kc, vc = _decode_rope_case(dev, case, seed=sum(case) % 991)
+    _check_rope_step(w, case[5], q, k, v, kn, ref, got, kc, vc, str(case))
+
+
+def test_decode_rope_append_large_angles(dev):
+    """Angles far from zero for every pair (positions scaled by 1e3): the
+    rotation is then far from the identity in every dimension."""
+    case = (3, 12, 2, 128, 700, 613, 0)
+    w, (q, k, v, kn), ref, got, kc, vc = _decode_rope_case(dev, case, seed=5,
+                                                           scale_angles=1000.0)
+    _check_rope_step(w, case[5], q, k, v, kn, ref, got, kc, vc, "large angles")
+
+
+def test_decode_rope_append_angle_zero_is_plain_step(dev):
+    """cos = 1, sin = 0 turns nothing: outputs and caches equal the plain
+    decode step's bit for bit."""
+    b, hq, hkv, d, ms, pos, win = 2, 12, 2, 128, 500, 411, 0
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, pos + 1, window=win, seed=77)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=78)
+    ones = torch.ones(d // 2, device=dev)
+    zeros = torch.zeros(d // 2, device=dev)
+    ws = A.decode_workspace(b, hq, hkv, d, pos + 1, win)
+    res = []
+    for rope in (False, True):
+        kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+        out = torch.full((b, hq, d), float("nan"), device=dev)
+        args = (torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
+                torch.from_numpy(vn).to(dev))
+        if rope:
+            A.attn_decode_rope_append(*args, ones, zeros, kd, vd, out, b, hq, hkv, d, ms,
+                                      pos, win, w.scale, ws)
+        else:
+            A.attn_decode_append(*args, kd, vd, out, b, hq, hkv, d, ms, pos, win, w.scale, ws)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), kd.cpu().numpy(), vd.cpu().numpy()))
+    for a, r in zip(res[0], res[1]):
+        assert np.array_equal(a, r)
+
+
+def test_decode_rope_append_no_heads_appends_rotated_rows(dev):
+    """num_heads == 0: nothing to attend, the rotated K row and the V row are
+    still appended."""
+    b, hkv, d, ms, pos = 3, 4, 64, 20, 17
+    ks, vs = synth.append_inputs(b, hkv, d, seed=3)
+    cos_t, sin_t = synth.rope_tables(d, 123.0)
+    kc = torch.full((b, hkv, ms, d), -1.5, device=dev)
+    vc = torch.full((b, hkv, ms, d), 0.75, device=dev)
+    A.attn_decode_rope_append(0, torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev),
+                              torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev),
+                              kc, vc, 0, b, 0, hkv, d, ms, pos, 0, 0.125, None)
+    torch.cuda.synchronize()
+    kn, vn = kc.cpu().numpy(), vc.cpu().numpy()
+    assert np.array_equal(vn[:, :, pos], vs)
+    err = np.abs(kn[:, :, pos].astype(np.float64) - oracle.rope(ks, cos_t, sin_t))
+    assert np.all(err <= _rope_row_bound(ks)), float(err.max())
+    keep = np.arange(ms) != pos
+    assert np.all(kn[:, :, keep] == -1.5) and np.all(vn[:, :, keep] == 0.75)
+
+
+def test_decode_rope_append_full_decode_workload(dev):
+    """The decode workload's shape (32 x 12 heads, 4096 positions) as a
+    rotary decode step at position 4095."""
+    w0 = synth.WORKLOADS["decode_b32_hq12_hkv2_d128_t4096"]
+    case = (w0.batch, w0.num_heads, w0.kv_heads, w0.head_dim, w0.max_seq, 4095, 0)
+    w, (q, k, v, kn), ref, got, kc, vc = _decode_rope_case(dev, case, seed=w0.seed)
+    _check_rope_step(w, 4095, q, k, v, kn, ref, got, kc, vc, "rotary decode step")
 
 
 # --------------------------------------------------------------- kv append
