@@ -75,6 +75,11 @@ def _bind(lib):
     lib.oracle_kv_append.argtypes = [
         _F32P, _F32P, _F32P, _F32P, ctypes.c_uint32, ctypes.c_uint32,
         ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+    lib.oracle_kv_append_rows.restype = ctypes.c_int
+    lib.oracle_kv_append_rows.argtypes = [_F32P] * 4 + [ctypes.c_uint32] * 6
+    lib.oracle_decode_varlen.restype = ctypes.c_int
+    lib.oracle_decode_varlen.argtypes = [_F32P] * 3 + [_U32P] + [ctypes.c_uint32] * 6 + [
+        ctypes.c_float, _F64P]
     return lib
 
 
@@ -181,6 +186,43 @@ class Oracle:
             raise ValueError("oracle_kv_append rejected its arguments")
 
 
+    def kv_append_rows(self, k_src, v_src, k_cache, v_cache, m, kv_stride, kv_heads,
+                       head_dim, max_seq, position) -> None:
+        """Write m prefill rows ([m, kv_stride] packed K/V) into one sequence's
+        caches ([kv_heads, max_seq, head_dim]) from row ``position`` on."""
+        n_cache = kv_heads * max_seq * head_dim
+        if k_cache.size < n_cache or v_cache.size < n_cache:
+            raise ValueError("cache arrays smaller than the stated shape")
+        if m and (k_src.size < (m - 1) * kv_stride + kv_heads * head_dim
+                  or v_src.size < (m - 1) * kv_stride + kv_heads * head_dim):
+            raise ValueError("source arrays smaller than the stated shape")
+        rc = self._lib.oracle_kv_append_rows(
+            _f32(k_src, "k_src"), _f32(v_src, "v_src"),
+            _f32(k_cache, "k_cache", True), _f32(v_cache, "v_cache", True),
+            m, kv_stride, kv_heads, head_dim, max_seq, position)
+        if rc != 0:
+            raise ValueError("oracle_kv_append_rows rejected its arguments")
+
+    def decode_varlen(self, q, k_cache, v_cache, seq_lens, batch, num_heads, kv_heads,
+                      head_dim, max_seq, window, scale):
+        """Decode with per-sequence lengths ``seq_lens`` ([batch] ints); a
+        length-0 sequence gives zeros. Returns [B, Hq, d] float64."""
+        n_cache = batch * kv_heads * max_seq * head_dim
+        if (q.size < batch * num_heads * head_dim or k_cache.size < n_cache
+                or v_cache.size < n_cache):
+            raise ValueError("input arrays smaller than the stated shapes")
+        lens = np.ascontiguousarray(seq_lens, dtype=np.uint32)
+        if lens.size < batch:
+            raise ValueError("seq_lens shorter than the batch")
+        out = np.empty((batch, num_heads, head_dim), dtype=np.float64)
+        rc = self._lib.oracle_decode_varlen(
+            _f32(q, "q"), _f32(k_cache, "k_cache"), _f32(v_cache, "v_cache"),
+            lens.ctypes.data_as(_U32P), batch, num_heads, kv_heads, head_dim, max_seq,
+            window, ctypes.c_float(scale), out.ctypes.data_as(_F64P))
+        if rc != 0:
+            raise ValueError("oracle_decode_varlen rejected its arguments")
+        return out
+
     def rope(self, x, cos_t, sin_t):
         """Rotate-half rotary embedding of the rows of x ([..., d] float32)
         with per-pair cos/sin ([d/2] float32); returns float64."""
@@ -245,6 +287,14 @@ def decode(*args, **kw) -> np.ndarray:
 
 def kv_append(*args, **kw) -> None:
     return default().kv_append(*args, **kw)
+
+
+def kv_append_rows(*args, **kw) -> None:
+    return default().kv_append_rows(*args, **kw)
+
+
+def decode_varlen(*args, **kw) -> np.ndarray:
+    return default().decode_varlen(*args, **kw)
 
 
 def rope(*args, **kw) -> np.ndarray:

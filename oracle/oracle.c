@@ -231,6 +231,87 @@ int oracle_kv_append(const float *k_src, const float *v_src, float *k_cache,
     return 0;
 }
 
+/*
+ * Bulk append of the K and V rows of a prefill pass into the caches (the
+ * page's KV-append kernels, taken over M rows of the prefill's packed K/V
+ * layout): for j < m and every KV head g,
+ *   cache[g, position + j, :] = src[j * kv_stride + g * head_dim + (0..d-1)].
+ * src: [m, kv_stride]; caches: [kv_heads, max_seq, head_dim] (one sequence).
+ */
+int oracle_kv_append_rows(const float *k_src, const float *v_src, float *k_cache,
+                          float *v_cache, uint32_t m, uint32_t kv_stride,
+                          uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                          uint32_t position)
+{
+    if ((uint64_t)position + m > max_seq ||
+        (uint64_t)kv_stride < (uint64_t)kv_heads * head_dim)
+        return -1;
+    for (uint32_t j = 0; j < m; ++j)
+        for (uint32_t g = 0; g < kv_heads; ++g) {
+            size_t src = (size_t)j * kv_stride + (size_t)g * head_dim;
+            size_t dst = ((size_t)g * max_seq + position + j) * head_dim;
+            for (uint32_t e = 0; e < head_dim; ++e) {
+                k_cache[dst + e] = k_src[src + e];
+                v_cache[dst + e] = v_src[src + e];
+            }
+        }
+    return 0;
+}
+
+/*
+ * Decode of a batch whose sequences have their own lengths: sequence b
+ * attends its rows [w0_b, seq_lens[b]) with w0_b from the page's window rule
+ * applied to seq_lens[b]. A sequence of length 0 attends nothing and its
+ * outputs are 0 (an idle batch slot). Lengths above max_seq are rejected.
+ * Shapes as oracle_decode; out: [batch, num_heads, head_dim] doubles.
+ */
+int oracle_decode_varlen(const float *q, const float *k_cache, const float *v_cache,
+                         const uint32_t *seq_lens, uint32_t batch,
+                         uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                         uint32_t max_seq, uint32_t window, float scale,
+                         double *out)
+{
+    if (kv_heads == 0 || head_dim == 0 || num_heads % kv_heads)
+        return -1;
+    for (uint32_t b = 0; b < batch; ++b)
+        if (seq_lens[b] > max_seq)
+            return -1;
+    uint32_t repeat = num_heads / kv_heads;
+    size_t total = (size_t)batch * num_heads;
+    int bad = 0;
+
+#pragma omp parallel
+    {
+        double *scores = (double *)malloc(sizeof(double) * (max_seq ? max_seq : 1));
+        if (!scores) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (size_t t = 0; t < total; ++t) {
+            if (!scores)
+                continue;
+            uint32_t b = (uint32_t)(t / num_heads);
+            uint32_t h = (uint32_t)(t % num_heads);
+            uint32_t len = seq_lens[b];
+            double *o = out + t * head_dim;
+            if (len == 0) {
+                for (uint32_t e = 0; e < head_dim; ++e)
+                    o[e] = 0.0;
+                continue;
+            }
+            uint32_t w0 = (window > 0 && len > window) ? len - window : 0;
+            uint32_t g = h / repeat;
+            const float *qh = q + ((size_t)b * num_heads + h) * head_dim;
+            size_t base = (((size_t)b * kv_heads + g) * max_seq + w0) * head_dim;
+            attend(qh, k_cache + base, v_cache + base, head_dim, (size_t)(len - w0),
+                   head_dim, (double)scale, scores, o);
+        }
+        free(scores);
+    }
+    return bad ? -1 : 0;
+}
+
 /* Rotate-half rotary embedding of one vector of d elements (d even), in fp64
  * on the fp32 input; out may not alias x. */
 static void rope(const float *x, const float *cs, const float *sn, uint32_t d,

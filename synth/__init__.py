@@ -183,6 +183,21 @@ def append_inputs(batch: int, kv_heads: int, head_dim: int, seed: int,
     return k, v
 
 
+def seq_lengths(batch: int, max_len: int, seed: int, min_len: int = 1,
+                idle: int = 0):
+    """Per-sequence lengths ``[batch]`` uint32 for a mixed-length decode
+    batch: uniform in [min_len, max_len], the longest forced to max_len
+    (so the batch bound is reached), and ``idle`` slots of length 0."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(min_len, max_len + 1, size=batch).astype(np.uint32)
+    if batch:
+        lens[int(rng.integers(batch))] = max_len
+    if idle:
+        free = np.flatnonzero(lens != max_len)
+        lens[rng.choice(free, size=min(idle, free.size), replace=False)] = 0
+    return lens
+
+
 def rope_tables(head_dim: int, position: int, base: float = 10000.0):
     """cos/sin tables ``[head_dim/2]`` float32 for one position: pair i turns
     by position * base^(-2i/head_dim) (the usual geometric frequency

@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle as pins
 from tests import test_oracle_rope as rope_pins
+from tests import test_oracle_serving as serving_pins
 
 MUTANTS = {
     "gqa_interleaved_prefill": ("uint32_t g = h / heads_per_kv;",
@@ -50,6 +51,15 @@ MUTANTS = {
     "rope_sign": ("out[i] = a * c - b * s;", "out[i] = a * c + b * s;"),
     "rope_pair_index": ("double a = x[i], b = x[i + half]", "double a = x[i], b = x[half - 1 - i]"),
     "rope_step_raw_k": ("dot += qh[e] * kn[e];", "dot += qh[e] * (double)k_raw[((size_t)b * kv_heads + g) * d + e];"),
+    "rows_src_ignores_stride": ("size_t src = (size_t)j * kv_stride + (size_t)g * head_dim;",
+                                "size_t src = (size_t)j * kv_heads * head_dim + (size_t)g * head_dim;"),
+    "rows_dst_row_major": ("size_t dst = ((size_t)g * max_seq + position + j) * head_dim;",
+                           "size_t dst = ((size_t)j * kv_heads + g + position) * head_dim;"),
+    "rows_v_from_k": ("v_cache[dst + e] = v_src[src + e];\n            }\n        }\n    return 0;\n}\n\n/*\n * Decode of a batch",
+                      "v_cache[dst + e] = k_src[src + e];\n            }\n        }\n    return 0;\n}\n\n/*\n * Decode of a batch"),
+    "varlen_first_length": ("uint32_t len = seq_lens[b];", "uint32_t len = seq_lens[0];"),
+    "varlen_window_ignored": ("(window > 0 && len > window)", "(0 && len > window)"),
+    "varlen_idle_skipped": ("o[e] = 0.0;", "o[e] = o[e];"),
 }
 
 PIN_CALLS = [
@@ -76,6 +86,12 @@ PIN_CALLS = [
     ("rope_norms", lambda o, g: rope_pins.test_rope_preserves_pair_norms_and_composes(o)),
     ("rope_relative", lambda o, g: rope_pins.test_rope_relative_position(o)),
     ("rope_step", lambda o, g: rope_pins.test_decode_rope_append_is_rotate_append_decode(o)),
+    ("rows_slice", lambda o, g: serving_pins.test_kv_append_rows_is_a_slice_copy(o)),
+    ("rows_bounds", lambda o, g: serving_pins.test_kv_append_rows_bounds(o)),
+    ("rows_prefill_decode", lambda o, g: serving_pins.test_prefill_then_bulk_append_then_decode(o)),
+    ("varlen_sdpa", lambda o, g: serving_pins.test_decode_varlen_matches_sdpa_per_sequence(o, 6)),
+    ("varlen_equal", lambda o, g: serving_pins.test_decode_varlen_equal_lengths_is_decode(o)),
+    ("varlen_indep", lambda o, g: serving_pins.test_decode_varlen_sequences_are_independent(o)),
 ]
 
 
