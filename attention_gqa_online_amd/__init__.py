@@ -24,6 +24,15 @@ import still succeeds, but the first call raises.
                             v_cache, out, batch, num_heads, kv_heads,
                             head_dim, max_seq, position, window, scale,
                             workspace, workspace_bytes=None, stream=None)
+    kv_append_rows(k_src, v_src, k_cache, v_cache, m, kv_stride, kv_heads,
+                   head_dim, max_seq, position, stream=None)
+    attn_decode_varlen(q, k_cache, v_cache, out, seq_lens, batch, num_heads,
+                       kv_heads, head_dim, max_seq, seq_bound, window, scale,
+                       workspace, workspace_bytes=None, stream=None)
+    attn_decode_append_varlen(q, k_new, v_new, k_cache, v_cache, out,
+                              positions, batch, num_heads, kv_heads, head_dim,
+                              max_seq, seq_bound, window, scale, workspace,
+                              workspace_bytes=None, stream=None)
     attn_status_string(status) -> str
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed, and
@@ -39,7 +48,8 @@ __all__ = [
     "AttnError", "ATTN_OK", "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED",
     "ATTN_ERR_HIP", "SO_PATH", "library", "attn_prefill_causal",
     "attn_decode_workspace_bytes", "attn_decode", "kv_append",
-    "attn_decode_append", "attn_decode_rope_append", "attn_status_string",
+    "attn_decode_append", "attn_decode_rope_append", "kv_append_rows",
+    "attn_decode_varlen", "attn_decode_append_varlen", "attn_status_string",
     "decode_workspace",
 ]
 
@@ -49,6 +59,7 @@ ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 
 EXPORTS = ("attn_prefill_causal", "attn_decode_workspace_bytes", "attn_decode",
            "kv_append", "attn_decode_append", "attn_decode_rope_append",
+           "kv_append_rows", "attn_decode_varlen", "attn_decode_append_varlen",
            "attn_status_string")
 
 
@@ -91,6 +102,14 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_rope_append.restype = ctypes.c_int
         lib.attn_decode_rope_append.argtypes = [_vp] * 8 + [_u32] * 7 + [
             ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        lib.kv_append_rows.restype = ctypes.c_int
+        lib.kv_append_rows.argtypes = [_vp] * 4 + [_u32] * 6 + [_vp]
+        lib.attn_decode_varlen.restype = ctypes.c_int
+        lib.attn_decode_varlen.argtypes = [_vp] * 5 + [_u32] * 7 + [
+            ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        lib.attn_decode_append_varlen.restype = ctypes.c_int
+        lib.attn_decode_append_varlen.argtypes = [_vp] * 7 + [_u32] * 7 + [
+            ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ctypes.c_int]
         _lib = lib
@@ -106,8 +125,10 @@ def _ptr(x, name: str, min_elems: int = 0):
     import torch
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name}: expected a torch tensor or an int address")
-    if x.dtype != torch.float32 and name != "workspace":
-        raise TypeError(f"{name}: expected float32, got {x.dtype}")
+    want = {"workspace": None, "seq_lens": torch.int32, "positions": torch.int32}.get(
+        name, torch.float32)
+    if want is not None and x.dtype != want:
+        raise TypeError(f"{name}: expected {want}, got {x.dtype}")
     if not x.is_cuda:
         raise ValueError(f"{name}: expected a GPU tensor")
     if not x.is_contiguous():
@@ -241,3 +262,50 @@ def attn_decode_rope_append(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache,
         batch, num_heads, kv_heads, head_dim, max_seq, position, window, float(scale),
         _ptr(workspace, "workspace"), int(workspace_bytes), _stream(stream))
     _check("attn_decode_rope_append", st)
+
+
+def kv_append_rows(k_src, v_src, k_cache, v_cache, m, kv_stride, kv_heads, head_dim,
+                   max_seq, position, stream=None) -> None:
+    """Write m prefill rows of packed K/V (``[m, kv_stride]``) into one
+    sequence's caches (``[kv_heads, max_seq, head_dim]``) from ``position``."""
+    n_src = (m - 1) * kv_stride + kv_heads * head_dim if m else 0
+    n_cache = kv_heads * max_seq * head_dim
+    st = library().kv_append_rows(
+        _ptr(k_src, "k_src", n_src), _ptr(v_src, "v_src", n_src),
+        _ptr(k_cache, "k_cache", n_cache), _ptr(v_cache, "v_cache", n_cache),
+        m, kv_stride, kv_heads, head_dim, max_seq, position, _stream(stream))
+    _check("kv_append_rows", st)
+
+
+def attn_decode_varlen(q, k_cache, v_cache, out, seq_lens, batch, num_heads, kv_heads,
+                       head_dim, max_seq, seq_bound, window, scale, workspace,
+                       workspace_bytes=None, stream=None) -> None:
+    """Decode with per-sequence lengths ``seq_lens`` (int32 device tensor,
+    read as uint32), each at most ``seq_bound``."""
+    n_cache = batch * kv_heads * max_seq * head_dim
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    st = library().attn_decode_varlen(
+        _ptr(q, "q", batch * num_heads * head_dim), _ptr(k_cache, "k_cache", n_cache),
+        _ptr(v_cache, "v_cache", n_cache), _ptr(out, "out", batch * num_heads * head_dim),
+        _ptr(seq_lens, "seq_lens", batch), batch, num_heads, kv_heads, head_dim, max_seq,
+        seq_bound, window, float(scale), _ptr(workspace, "workspace"), int(workspace_bytes),
+        _stream(stream))
+    _check("attn_decode_varlen", st)
+
+
+def attn_decode_append_varlen(q, k_new, v_new, k_cache, v_cache, out, positions, batch,
+                              num_heads, kv_heads, head_dim, max_seq, seq_bound, window,
+                              scale, workspace, workspace_bytes=None, stream=None) -> None:
+    """Decode step with per-sequence positions (int32 device tensor, read as
+    uint32): sequence b appends at positions[b] and attends up to it."""
+    n_src = batch * kv_heads * head_dim
+    n_cache = batch * kv_heads * max_seq * head_dim
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    st = library().attn_decode_append_varlen(
+        _ptr(q, "q", batch * num_heads * head_dim), _ptr(k_new, "k_new", n_src),
+        _ptr(v_new, "v_new", n_src), _ptr(k_cache, "k_cache", n_cache),
+        _ptr(v_cache, "v_cache", n_cache), _ptr(out, "out", batch * num_heads * head_dim),
+        _ptr(positions, "positions", batch), batch, num_heads, kv_heads, head_dim, max_seq,
+        seq_bound, window, float(scale), _ptr(workspace, "workspace"), int(workspace_bytes),
+        _stream(stream))
+    _check("attn_decode_append_varlen", st)

@@ -12,6 +12,7 @@ namespace {
 bool head_dim_multiple_of_32(uint32_t d) { return d != 0 && d % 32 == 0; }
 bool head_dim_built(uint32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
@@ -55,8 +56,13 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads, uint32_t 
     if (kv_heads == 0 || num_heads % kv_heads != 0 || total_seq == 0) return 0;
     if (batch == 0 || num_heads == 0) return 0;
     if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return 0;
-    return attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window)
-        .workspace_bytes;
+    // large enough for every decode entry point's plan of these shapes
+    const size_t a =
+        attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window).workspace_bytes;
+    const size_t b = attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window,
+                                       false, true)
+                         .workspace_bytes;
+    return a > b ? a : b;
 }
 
 attn_status attn_decode(const float *q, const float *k_cache, const float *v_cache, float *out,
@@ -170,6 +176,86 @@ attn_status kv_append(const float *k_src, const float *v_src, float *k_cache, fl
         return ATTN_ERR_INVALID;
     return from_hip(attn::launch_kv_append(k_src, v_src, k_cache, v_cache, batch, kv_heads,
                                            head_dim, max_seq, position, stream));
+}
+
+attn_status kv_append_rows(const float *k_src, const float *v_src, float *k_cache,
+                           float *v_cache, uint32_t m, uint32_t kv_stride, uint32_t kv_heads,
+                           uint32_t head_dim, uint32_t max_seq, uint32_t position,
+                           hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim)) return ATTN_ERR_INVALID;
+    if ((uint64_t)position + m > max_seq) return ATTN_ERR_INVALID;
+    if (m == 0 || kv_heads == 0) return ATTN_OK;
+    if (kv_stride % 4 != 0 || (uint64_t)kv_stride < (uint64_t)kv_heads * head_dim)
+        return ATTN_ERR_INVALID;
+    if ((uint64_t)m * (head_dim / 4) > 0x7fffffffu || kv_heads > 65535u)
+        return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_INVALID;
+    return from_hip(attn::launch_kv_append_rows(k_src, v_src, k_cache, v_cache, m, kv_stride,
+                                                kv_heads, head_dim, max_seq, position, stream));
+}
+
+attn_status attn_decode_varlen(const float *q, const float *k_cache, const float *v_cache,
+                               float *out, const uint32_t *seq_lens, uint32_t batch,
+                               uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                               uint32_t max_seq, uint32_t seq_bound, uint32_t window,
+                               float scale, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
+    if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
+    if (seq_bound == 0 || seq_bound > max_seq) return ATTN_ERR_INVALID;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 || num_heads == 0) return ATTN_OK;
+    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned4(seq_lens))
+        return ATTN_ERR_INVALID;
+    const attn::DecodePlan plan =
+        attn::plan_decode(batch, num_heads, kv_heads, head_dim, seq_bound, window, false, true);
+    if (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_INVALID;
+    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodeVarlen vl{seq_lens, 0, seq_bound, window};
+    return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
+                                        head_dim, max_seq, seq_bound, scale, workspace,
+                                        nullptr, stream, &vl));
+}
+
+attn_status attn_decode_append_varlen(const float *q, const float *k_new, const float *v_new,
+                                      float *k_cache, float *v_cache, float *out,
+                                      const uint32_t *positions, uint32_t batch,
+                                      uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                                      uint32_t max_seq, uint32_t seq_bound, uint32_t window,
+                                      float scale, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
+    if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
+    if (seq_bound == 0 || seq_bound > max_seq) return ATTN_ERR_INVALID;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0) return ATTN_OK;
+    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu ||
+        (uint64_t)batch * kv_heads * (head_dim / 4) > 0x7fffffffu)
+        return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned4(positions))
+        return ATTN_ERR_INVALID;
+    if (num_heads == 0) {  // nothing to attend: the appends alone
+        return from_hip(attn::launch_kv_append(k_new, v_new, k_cache, v_cache, batch, kv_heads,
+                                               head_dim, max_seq, seq_bound, stream, nullptr,
+                                               nullptr, positions));
+    }
+    if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
+    const attn::DecodePlan plan =
+        attn::plan_decode(batch, num_heads, kv_heads, head_dim, seq_bound, window, true, true);
+    if (plan.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes))
+        return ATTN_ERR_INVALID;
+    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, nullptr, nullptr};
+    const attn::DecodeVarlen vl{positions, 1, seq_bound, window};
+    return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
+                                        head_dim, max_seq, seq_bound, scale, workspace, &app,
+                                        stream, &vl));
 }
 
 }  // extern "C"

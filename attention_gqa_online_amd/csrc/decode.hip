@@ -8,6 +8,13 @@ namespace {
 constexpr int kDecodeWaves = 4;          // waves per workgroup
 constexpr int kPrefetch = 2;             // row steps in flight per wave
 constexpr int kTargetWorkgroups = 256;   // one workgroup per CU, streaming long ranges
+// Per-sequence lengths are only known on the device: the plan is made for the
+// bound, and splits past a shorter sequence's end exit at once. Shorter splits
+// (two workgroups per CU for a batch at the bound) keep more rows in flight
+// when many splits are empty; measured on a 32-sequence batch, 4096-row
+// bound: lengths uniform in [1, 4096] 47 -> 40 us, every length 4096
+// 49 -> 52 us, against the single-length target.
+constexpr int kTargetWorkgroupsVarlen = 512;
 constexpr int kMinRowsPerWave = 32;
 
 constexpr int lanes_per_row(int d) { return d == 32 ? 8 : 16; }
@@ -58,7 +65,8 @@ inline uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1)
 }  // namespace
 
 DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
-                       uint32_t head_dim, uint32_t total_seq, uint32_t window, bool append) {
+                       uint32_t head_dim, uint32_t total_seq, uint32_t window, bool append,
+                       bool varlen) {
     DecodePlan p{};
     if (kv_heads == 0 || num_heads < kv_heads) return p;  // no head: no work, no workspace
     const uint32_t hpk = num_heads / kv_heads;
@@ -77,7 +85,7 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     const uint32_t rpt = 64 / lanes_per_row((int)head_dim);
     const uint32_t step = kDecodeWaves * rpt;
     const uint32_t max_split = ceil_div(len, (uint64_t)kDecodeWaves * kMinRowsPerWave);
-    uint32_t n_split = ceil_div(kTargetWorkgroups, p.units);
+    uint32_t n_split = ceil_div(varlen ? kTargetWorkgroupsVarlen : kTargetWorkgroups, p.units);
     n_split = n_split > max_split ? max_split : n_split;
     n_split = n_split > (uint32_t)kMaxSplit ? (uint32_t)kMaxSplit : n_split;
     n_split = n_split < 1 ? 1 : n_split;
@@ -94,7 +102,8 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
                          const float *v_cache, float *out, uint32_t num_heads,
                          uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
                          uint32_t total_seq, float scale, void *workspace,
-                         const DecodeAppend *append, hipStream_t stream) {
+                         const DecodeAppend *append, hipStream_t stream,
+                         const DecodeVarlen *varlen) {
     DecodeArgs a{};
     a.q = q;
     a.k = k_cache;
@@ -119,6 +128,12 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
         a.position = total_seq - 1;
         a.cos_t = append->cos_t;
         a.sin_t = append->sin_t;
+    }
+    if (varlen) {  // total_seq is then the bound the plan was made for
+        a.lens = varlen->lens;
+        a.len_add = varlen->len_add;
+        a.seq_bound = varlen->seq_bound;
+        a.window = varlen->window;
     }
     const uint32_t hc = plan.head_chunk, u = plan.units, ns = plan.n_split;
     switch (head_dim) {

@@ -58,10 +58,33 @@ struct DecodeArgs {
     // cos/sin [D/2] for `position`, applied to q and to the new K rows
     const float *cos_t;
     const float *sin_t;
+    // per-sequence lengths, or null (then every sequence has the rows
+    // [w0, total_seq) before the appended one): sequence b then has
+    // T_b = lens[b] + len_add rows, valid when T_b <= seq_bound; with an
+    // append (len_add = 1, lens = positions) the new row is row T_b - 1
+    const uint32_t *lens;
+    uint32_t len_add, seq_bound, window;
     uint32_t num_heads, kv_heads, hpk, n_chunks, max_seq;
     uint32_t w0, total_seq, n_split, rows_per_split;
     float qscale;     // scale * log2(e): scores come out in log2 units
 };
+
+// Rows of sequence b: the split pass covers [w0, hi); `pos` is the appended
+// row. An invalid per-sequence length (past seq_bound) gives valid = false
+// and an empty range.
+struct SeqRange {
+    uint32_t w0, hi, pos;
+    bool valid;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, uint32_t b) {
+    if (a.lens == nullptr) return {a.w0, a.total_seq, a.position, true};
+    const uint64_t t = (uint64_t)a.lens[b] + a.len_add;
+    const bool valid = t <= a.seq_bound;
+    const uint32_t T = valid ? (uint32_t)t : 0;
+    const uint32_t w0 = (a.window > 0 && T > a.window) ? T - a.window : 0;
+    return {w0, T > 0 ? T - a.len_add : 0, T > 0 ? T - 1 : 0, valid};
+}
 
 template <bool NT>
 __device__ __forceinline__ float4 kv_load(const float *p) {
@@ -105,8 +128,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
     // rows of this workgroup, then of this wave: either a contiguous quarter
     // of the workgroup's range, or every NW-th step of it (INTERLEAVE)
-    const uint32_t ws0 = a.w0 + split * a.rows_per_split;
-    const uint32_t ws1 = min(ws0 + a.rows_per_split, a.total_seq);
+    const SeqRange sr = seq_range(a, b);
+    const uint32_t ws0 = sr.w0 + split * a.rows_per_split;
+    const uint32_t ws1 = min(ws0 + a.rows_per_split, sr.hi);
+    if constexpr (MERGE == kMergePartialOnly) {
+        // a split past a shorter sequence's end: nothing to write, the merge
+        // pass folds only the splits that hold rows (uniform per workgroup)
+        if (a.lens != nullptr && ws0 >= ws1) return;
+    }
     const uint32_t per_wave = a.rows_per_split / NW;
     const uint32_t ra = INTERLEAVE ? ws0 + wave * RPT : min(ws0 + wave * per_wave, ws1);
     const uint32_t rb = INTERLEAVE ? ws1 : min(ra + per_wave, ws1);
@@ -292,7 +321,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         if (d == 0 || MERGE == kMergeDirect)
             for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh] * s_f[sl][hh];
         if constexpr (MERGE == kMergeDirect) {
-            if (hh < nh) a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = x / lsum;
+            // no rows (an idle sequence): 0; an invalid length: NaN
+            const float o = !sr.valid ? __builtin_nanf("") : lsum > 0.f ? x / lsum : 0.f;
+            if (hh < nh) a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = o;
         } else {
             mypart[hh * (D + 2) + d] = x;
             if (d == 0) {
@@ -341,9 +372,19 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     const uint32_t hl0 = chunk * HC;
     if ((int)(a.hpk - hl0) <= hh) return;  // head past this chunk's end
     const uint32_t h = g * a.hpk + hl0 + hh;
-    const uint32_t ns = a.n_split;
+    const SeqRange sr = seq_range(a, b);
+    uint32_t ns = a.n_split;
+    if (a.lens != nullptr) {
+        if (!sr.valid) {  // invalid length: NaN output, nothing appended
+            a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
+            return;
+        }
+        // only the splits that start before this sequence's end hold rows
+        const uint32_t rows = sr.hi > sr.w0 ? sr.hi - sr.w0 : 0;
+        ns = ns == 0 ? 0 : (rows + a.rows_per_split - 1) / a.rows_per_split;
+    }
     constexpr uint32_t SS = HC * (D + 2);  // floats between splits
-    const float *up = a.part + (size_t)unit * ns * SS + hh * (D + 2);
+    const float *up = a.part + (size_t)unit * a.n_split * SS + hh * (D + 2);
 
     float M = kNegInf, num = 0.f, den = 0.f;
     if (a.k_new != nullptr) {
@@ -364,7 +405,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
         num = vn;
         den = 1.f;
         if (hl0 + hh == 0) {  // one writer per (sequence, KV head)
-            const size_t dst = ((size_t)bg * a.max_seq + a.position) * D + tid;
+            const size_t dst = ((size_t)bg * a.max_seq + sr.pos) * D + tid;
             a.k_dst[dst] = kn;
             a.v_dst[dst] = vn;
         }
@@ -393,7 +434,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
         }
         M = Mn;
     }
-    a.out[((size_t)b * a.num_heads + h) * D + tid] = num / den;
+    // den is 0 only for an idle sequence (no rows, nothing appended)
+    a.out[((size_t)b * a.num_heads + h) * D + tid] = den > 0.f ? num / den : 0.f;
 }
 
 }  // namespace attn

@@ -285,6 +285,79 @@ def bench_prefill(args, dev, name, device_inputs=True):
             "algorithmic_flops": w.flops()}
 
 
+def bench_decode_varlen(args, dev):
+    """Serving-shaped decode step: the decode workload's shape (32 sequences,
+    12 query / 2 KV heads of 128, caches of 4096 rows) with each sequence at
+    its own position, lengths uniform in [1, 4096] (seeded); one
+    attn_decode_append_varlen call per step."""
+    import numpy as np
+    import torch
+    import attention_gqa_online_amd as A
+    import synth
+    w = synth.WORKLOADS[HEADLINE]
+    lens = synth.seq_lengths(w.batch, w.total_seq, seed=w.seed + 100)
+    sets = [synth.decode_inputs_device(w, w.seed + 20 + r, dev) for r in range(3)]
+    kn, vn = (torch.from_numpy(x).to(dev)
+              for x in synth.append_inputs(w.batch, w.kv_heads, w.head_dim, seed=w.seed + 30))
+    pos = torch.from_numpy((lens - 1).astype(np.int32)).to(dev)
+    out = torch.empty(w.batch, w.num_heads, w.head_dim, device=dev)
+    ws = A.decode_workspace(w.batch, w.num_heads, w.kv_heads, w.head_dim, w.total_seq,
+                            w.window, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        q, k, v = sets[i % 3]
+        A.attn_decode_append_varlen(q, kn, vn, k, v, out, pos, w.batch, w.num_heads,
+                                    w.kv_heads, w.head_dim, w.max_seq, w.total_seq, w.window,
+                                    w.scale, ws)
+    ms, wall = time_calls(call, max(args.steps, 10), args.warmup, stream)
+    med = statistics.median(ms)
+    bytes_ = int(2 * w.kv_heads * w.head_dim * 4 * int(lens.astype(np.int64).sum()))
+    gbs = bytes_ / (med * 1e-3) / 1e9
+    del sets
+    torch.cuda.empty_cache()
+    log(f"[bench] varlen decode step: median {med * 1e3:.1f} us, {gbs:.0f} GB/s "
+        f"(mean length {lens.mean():.0f})")
+    return {"workload": "decode_varlen_b32_hq12_hkv2_d128_t4096_uniform",
+            "step": "attn_decode_append_varlen", "mean_len": round(float(lens.mean()), 1),
+            "median_us": round(med * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
+            "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "algorithmic_bytes": bytes_}
+
+
+def bench_append_rows(args, dev):
+    """Prefill -> cache hand-over at the long prefill's shape: 16384 rows of
+    8 KV heads x 128 into [8, 16384, 128] caches (K and V read once, written
+    once)."""
+    import torch
+    import attention_gqa_online_amd as A
+    m, hkv, d = 16384, 8, 128
+    g = torch.Generator(device=dev).manual_seed(7)
+    k = torch.randn((m, hkv * d), generator=g, device=dev)
+    v = torch.randn((m, hkv * d), generator=g, device=dev)
+    caches = [(torch.empty((hkv, m, d), device=dev), torch.empty((hkv, m, d), device=dev))
+              for _ in range(2)]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        kc, vc = caches[i % 2]
+        A.kv_append_rows(k, v, kc, vc, m, hkv * d, hkv, d, m, 0)
+    ms, wall = time_calls(call, max(args.steps, 10), args.warmup, stream)
+    med = statistics.median(ms)
+    bytes_ = 4 * m * hkv * d * 4
+    gbs = bytes_ / (med * 1e-3) / 1e9
+    del k, v, caches
+    torch.cuda.empty_cache()
+    log(f"[bench] kv_append_rows: median {med * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": "append_rows_m16384_hkv8_d128", "median_us": round(med * 1e3, 2),
+            "min_us": round(min(ms) * 1e3, 2), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "algorithmic_bytes": bytes_}
+
+
 def copy_calibration(dev, mib=256, reps=3):
     """A plain device copy of known size, for scaling HBM byte counters: each
     copy reads and writes exactly `mib` MiB."""
@@ -304,7 +377,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--modes", default="headline,decode_window,prefill_long,prefill_qwen,prefill_tiny",
+    ap.add_argument("--modes", default="headline,decode_window,decode_varlen,append_rows,"
+                                       "prefill_long,prefill_qwen,prefill_tiny",
                     help="comma list; the headline decode step always runs "
                          "(also: copy_calibration)")
     args = ap.parse_args()
@@ -328,6 +402,10 @@ def main():
     extra = {"decode_step_two_calls": two, "decode_step_rope": rope}
     if "decode_window" in modes:
         extra["decode_window"] = bench_decode_window(args, dev)
+    if "decode_varlen" in modes:
+        extra["decode_varlen"] = bench_decode_varlen(args, dev)
+    if "append_rows" in modes:
+        extra["append_rows"] = bench_append_rows(args, dev)
     if "prefill_long" in modes:
         extra["prefill_long"] = bench_prefill(args, dev, "prefill_hq64_hkv8_d128_m16384")
     if "prefill_qwen" in modes:

@@ -14,6 +14,11 @@
  *   attn_decode_rope_append
  *                         the same decode step with rotary position embedding
  *                         applied to q and to the new K rows on the way in
+ *   kv_append_rows        write a prefill pass's K and V rows into a
+ *                         sequence's caches (prefill -> decode hand-over)
+ *   attn_decode_varlen    attn_decode with one length per sequence
+ *   attn_decode_append_varlen
+ *                         attn_decode_append with one position per sequence
  *
  * Common rules
  *   - Every tensor is fp32, row-major. Every pointer is a DEVICE pointer owned
@@ -224,6 +229,94 @@ attn_status kv_append(const float *k_src, const float *v_src, float *k_cache,
                       float *v_cache, uint32_t batch, uint32_t kv_heads,
                       uint32_t head_dim, uint32_t max_seq, uint32_t position,
                       hipStream_t stream);
+
+/*
+ * Bulk append of a prefill pass's K and V rows into one sequence's caches
+ * (glia honeycrisp "attention.rs" page, the KV-append kernels, taken over the
+ * m rows of the packed K/V layout of aprender-gpu 0.32.0 "prefill_fused.rs"
+ * page, the kernel's buffer parameters), so that decode can follow prefill.
+ *
+ *   k_src, v_src      [m, kv_stride]   KV head g at columns g*head_dim ..
+ *                                      (the layout attn_prefill_causal reads)
+ *   k_cache, v_cache  [kv_heads, max_seq, head_dim]  one sequence's caches
+ *                     (for a batch slot b of [batch, kv_heads, max_seq,
+ *                     head_dim] caches, pass the slot's base address)
+ *
+ * k_cache[g, position + j, :] = k_src[j, g*head_dim : (g+1)*head_dim] for
+ * j < m and every g, the same for V; no other element is written. One
+ * launch. Sources must not overlap the caches.
+ *
+ * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, position + m > max_seq,
+ * kv_stride < kv_heads*head_dim or not a multiple of 4, or a null /
+ * misaligned pointer; ATTN_ERR_UNSUPPORTED if m*head_dim/4 >= 2^31 or
+ * kv_heads > 65535. m == 0 or kv_heads == 0 returns ATTN_OK without a launch.
+ */
+attn_status kv_append_rows(const float *k_src, const float *v_src, float *k_cache,
+                           float *v_cache, uint32_t m, uint32_t kv_stride,
+                           uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
+                           uint32_t position, hipStream_t stream);
+
+/*
+ * Decode of a batch whose sequences have their own lengths (the decode
+ * Params struct of glia honeycrisp "attention.rs" page carries one
+ * total_seq; here there is one per sequence, read by the kernels from
+ * device memory, so a serving loop can change them without a host sync).
+ *
+ *   seq_lens   [batch] uint32, DEVICE memory: T_b, the rows of sequence b
+ *   seq_bound  host-side bound on every T_b, 1 <= seq_bound <= max_seq; the
+ *              work split and the workspace are sized for it
+ *   other arguments as attn_decode.
+ *
+ * Sequence b attends rows [w0_b, T_b), w0_b = (window > 0 && T_b > window)
+ * ? T_b - window : 0. Device-side lengths cannot be checked before the
+ * launch, so the kernels define the rest: T_b == 0 (an idle batch slot)
+ * gives out[b] = 0, and T_b > seq_bound gives out[b] = NaN with no cache
+ * row read.
+ *
+ * workspace: at least attn_decode_workspace_bytes(batch, num_heads,
+ * kv_heads, head_dim, seq_bound, window) bytes, contents irrelevant.
+ *
+ * Errors: as attn_decode with total_seq replaced by seq_bound, plus a null
+ * or misaligned (4-byte) seq_lens. batch == 0 or num_heads == 0 returns
+ * ATTN_OK without a launch.
+ */
+attn_status attn_decode_varlen(const float *q, const float *k_cache,
+                               const float *v_cache, float *out,
+                               const uint32_t *seq_lens, uint32_t batch,
+                               uint32_t num_heads, uint32_t kv_heads,
+                               uint32_t head_dim, uint32_t max_seq,
+                               uint32_t seq_bound, uint32_t window, float scale,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * One decode step of a batch whose sequences sit at their own positions:
+ * sequence b appends its new K and V rows at positions[b] and attends rows
+ * [w0_b, positions[b]] (T_b = positions[b] + 1, window rule as above); the
+ * batched form of attn_decode_append.
+ *
+ *   positions  [batch] uint32, DEVICE memory
+ *   seq_bound  host-side bound: every positions[b] + 1 <= seq_bound <= max_seq
+ *   other arguments as attn_decode_append.
+ *
+ * A sequence with positions[b] + 1 > seq_bound gets out[b] = NaN and no
+ * cache write. workspace: at least attn_decode_workspace_bytes(batch,
+ * num_heads, kv_heads, head_dim, seq_bound, window) bytes (may be null when
+ * that size is 0).
+ *
+ * Errors: as attn_decode_append with position + 1 replaced by seq_bound,
+ * plus a null or misaligned (4-byte) positions. batch == 0 returns ATTN_OK
+ * without a launch; num_heads == 0 only appends.
+ */
+attn_status attn_decode_append_varlen(const float *q, const float *k_new,
+                                      const float *v_new, float *k_cache,
+                                      float *v_cache, float *out,
+                                      const uint32_t *positions, uint32_t batch,
+                                      uint32_t num_heads, uint32_t kv_heads,
+                                      uint32_t head_dim, uint32_t max_seq,
+                                      uint32_t seq_bound, uint32_t window,
+                                      float scale, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char *attn_status_string(attn_status s);

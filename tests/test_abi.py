@@ -198,3 +198,69 @@ def test_decode_rope_append_argument_rules(lib):
     assert _decode_rope(lib, ws=0) == INVALID
     assert _decode_rope(lib, b=0) == OK                            # no work, no launch
     assert _decode_rope(lib, b=0, ptrs=(0,) * 8) == OK
+
+
+def test_kv_append_rows_argument_rules(lib):
+    f = lib.kv_append_rows
+    #        k  v  kc vc  m  stride hkv  d  max_seq pos
+    assert f(P, P, P, P, 4, 256, 2, 48, 16, 0, None) == INVALID        # d % 32
+    assert f(P, P, P, P, 4, 256, 2, 128, 16, 13, None) == INVALID      # past the cache
+    assert f(P, P, P, P, 4, 255, 2, 128, 16, 0, None) == INVALID       # stride too small
+    assert f(P, P, P, P, 4, 258, 2, 128, 16, 0, None) == INVALID       # stride % 4
+    assert f(P, P, 0, P, 4, 256, 2, 128, 16, 0, None) == INVALID
+    assert f(P, P + 8, P, P, 4, 256, 2, 128, 16, 0, None) == INVALID
+    assert f(P, P, P, P, 1 << 26, 256, 2, 128, 1 << 27, 0, None) == UNSUPPORTED
+    assert f(0, 0, 0, 0, 0, 256, 2, 128, 16, 16, None) == OK           # no rows
+    assert f(0, 0, 0, 0, 4, 256, 0, 128, 16, 0, None) == OK            # no heads
+    assert f(P, P, P, P, 4, 256, 2, 128, 16, 13, None) == INVALID
+
+
+def _varlen(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, bound=64, window=0,
+            scale=0.088, ws=P, ws_bytes=1 << 30, ptrs=(P,) * 5):
+    return lib.attn_decode_varlen(*ptrs, b, hq, hkv, d, max_seq, bound, window,
+                                  ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+def test_decode_varlen_argument_rules(lib):
+    assert _varlen(lib, d=48) == INVALID
+    assert _varlen(lib, d=96) == UNSUPPORTED
+    assert _varlen(lib, hkv=0) == INVALID
+    assert _varlen(lib, hq=12, hkv=5) == INVALID
+    assert _varlen(lib, bound=0) == INVALID
+    assert _varlen(lib, bound=65, max_seq=64) == INVALID
+    assert _varlen(lib, scale=float("nan")) == INVALID
+    for i in range(4):
+        ptrs = tuple(P + 4 if j == i else P for j in range(5))
+        assert _varlen(lib, ptrs=ptrs) == INVALID, i
+    assert _varlen(lib, ptrs=(P, P, P, P, 0)) == INVALID               # no lengths
+    assert _varlen(lib, ptrs=(P, P, P, P, P + 2)) == INVALID
+    need = lib.attn_decode_workspace_bytes(2, 12, 2, 128, 64, 0)
+    assert _varlen(lib, ws_bytes=need - 1) == INVALID
+    assert _varlen(lib, ws=0) == INVALID
+    assert _varlen(lib, b=0) == OK
+    assert _varlen(lib, hq=0) == OK
+
+
+def _append_varlen(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, bound=64, window=0,
+                   scale=0.088, ws=P, ws_bytes=1 << 30, ptrs=(P,) * 7):
+    return lib.attn_decode_append_varlen(*ptrs, b, hq, hkv, d, max_seq, bound, window,
+                                         ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+def test_decode_append_varlen_argument_rules(lib):
+    assert _append_varlen(lib, d=48) == INVALID
+    assert _append_varlen(lib, d=160) == UNSUPPORTED
+    assert _append_varlen(lib, hkv=0) == INVALID
+    assert _append_varlen(lib, bound=0) == INVALID
+    assert _append_varlen(lib, bound=65, max_seq=64) == INVALID
+    assert _append_varlen(lib, scale=float("inf")) == INVALID
+    for i in range(6):
+        for bad in (0, P + 4):
+            ptrs = tuple(bad if j == i else P for j in range(7))
+            assert _append_varlen(lib, ptrs=ptrs) == INVALID, (i, bad)
+    assert _append_varlen(lib, ptrs=(P,) * 6 + (0,)) == INVALID
+    assert _append_varlen(lib, ptrs=(P,) * 6 + (P + 1,)) == INVALID
+    need = lib.attn_decode_workspace_bytes(2, 12, 2, 128, 64, 0)
+    assert _append_varlen(lib, ws_bytes=need // 2) == INVALID
+    assert _append_varlen(lib, b=0) == OK
+    assert _append_varlen(lib, b=0, ptrs=(0,) * 7) == OK

@@ -401,6 +401,233 @@ def test_kv_append_full_size_window_workload(dev):
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------- bulk append (prefill rows)
+
+ROWS_CASES = [
+    # (m, kv_heads, head_dim, pad, max_seq, position)
+    (1, 1, 32, 0, 1, 0),
+    (17, 2, 32, 4, 40, 3),
+    (65, 4, 64, 0, 65, 0),
+    (300, 3, 128, 8, 512, 211),
+    (129, 1, 256, 4, 130, 1),
+    (2048, 4, 128, 0, 4096, 0),          # the Qwen-shaped prefill's K/V
+]
+
+
+@pytest.mark.parametrize("case", ROWS_CASES, ids=lambda c: "m{}_hkv{}_d{}_pad{}_ms{}_p{}".format(*c))
+def test_kv_append_rows_bit_exact(dev, case):
+    m, hkv, d, pad, ms, pos = case
+    rng = np.random.default_rng(m + d)
+    stride = hkv * d + pad
+    k = rng.standard_normal((m, stride), dtype=np.float32)
+    v = rng.standard_normal((m, stride), dtype=np.float32)
+    kc = torch.full((hkv, ms, d), -7.5, device=dev)
+    vc = torch.full((hkv, ms, d), 8.25, device=dev)
+    A.kv_append_rows(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), kc, vc, m,
+                     stride, hkv, d, ms, pos)
+    torch.cuda.synchronize()
+    kr = np.full((hkv, ms, d), -7.5, np.float32)
+    vr = np.full((hkv, ms, d), 8.25, np.float32)
+    oracle.kv_append_rows(k, v, kr, vr, m, stride, hkv, d, ms, pos)
+    assert np.array_equal(kc.cpu().numpy(), kr) and np.array_equal(vc.cpu().numpy(), vr)
+
+
+def test_kv_append_rows_long_prefill_shape(dev):
+    """The long prefill's K/V (16384 rows, 8 KV heads of 128) into caches
+    sized for 20000 rows; checked on the GPU against a gather of the source."""
+    m, hkv, d, ms = 16384, 8, 128, 20000
+    g = torch.Generator(device=dev).manual_seed(5)
+    k = torch.randn((m, hkv * d), generator=g, device=dev)
+    v = torch.randn((m, hkv * d), generator=g, device=dev)
+    kc = torch.full((hkv, ms, d), 3.0, device=dev)
+    vc = torch.full((hkv, ms, d), 4.0, device=dev)
+    A.kv_append_rows(k, v, kc, vc, m, hkv * d, hkv, d, ms, 7)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, 7:7 + m], k.view(m, hkv, d).permute(1, 0, 2))
+    assert torch.equal(vc[:, 7:7 + m], v.view(m, hkv, d).permute(1, 0, 2))
+    assert bool((kc[:, :7] == 3.0).all()) and bool((kc[:, 7 + m:] == 3.0).all())
+    assert bool((vc[:, :7] == 4.0).all()) and bool((vc[:, 7 + m:] == 4.0).all())
+
+
+def test_prefill_then_append_rows_then_decode(dev):
+    """GPU prefill over a fused QKV buffer, its K/V rows appended to a cache,
+    then GPU decode of Q row i over the first i+1 rows equals prefill row i."""
+    m, hq, hpk, d = 300, 12, 6, 128
+    hkv = hq // hpk
+    stride = (hq + 2 * hkv) * d
+    rng = np.random.default_rng(11)
+    qkv = rng.standard_normal((m, stride), dtype=np.float32)
+    buf = torch.from_numpy(qkv).to(dev)
+    q, k, v = buf[:, :hq * d], buf[:, hq * d:(hq + hkv) * d], buf[:, (hq + hkv) * d:]
+    o = torch.full((m, stride), float("nan"), device=dev)
+    A.attn_prefill_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), m, stride,
+                          stride, hq, hpk, d)
+    ms = 320
+    kc = torch.full((1, hkv, ms, d), float("nan"), device=dev)
+    vc = torch.full((1, hkv, ms, d), float("nan"), device=dev)
+    A.kv_append_rows(k.data_ptr(), v.data_ptr(), kc, vc, m, stride, hkv, d, ms, 0)
+    scale = 1.0 / np.sqrt(np.float32(d))
+    for i in (0, 63, 64, m - 1):
+        qi = q[i].reshape(1, hq, d).contiguous()
+        out = torch.full((1, hq, d), float("nan"), device=dev)
+        ws = A.decode_workspace(1, hq, hkv, d, i + 1, 0)
+        A.attn_decode(qi, kc, vc, out, 1, hq, hkv, d, ms, i + 1, 0, float(scale), ws)
+        torch.cuda.synchronize()
+        ref = oracle.prefill_causal(qkv[:, :hq * d].copy(), qkv[:, hq * d:(hq + hkv) * d].copy(),
+                                    qkv[:, (hq + hkv) * d:].copy(), m, hq * d, hkv * d, hq, hpk,
+                                    d, rows=np.full(hq, i, np.uint32),
+                                    heads=np.arange(hq, dtype=np.uint32))
+        vmax = float(np.abs(qkv[:i + 1, (hq + hkv) * d:]).max())
+        got_p = o[i, :hq * d].cpu().numpy().reshape(hq, d)
+        got_d = out[0].cpu().numpy()
+        _assert_close(got_p, ref.reshape(hq, d), vmax, f"prefill row {i}")
+        _assert_close(got_d, ref.reshape(hq, d), vmax, f"decode row {i}")
+
+
+# -------------------------------------------------------------- varlen decode
+
+VARLEN_CASES = [
+    # (batch, hq, hkv, d, max_seq, bound, window, idle)
+    (6, 12, 2, 128, 300, 300, 0, 1),
+    (5, 8, 8, 64, 100, 77, 9, 1),        # MHA, window below most lengths
+    (7, 4, 2, 32, 50, 50, 0, 2),
+    (3, 16, 2, 256, 700, 650, 100, 0),
+    (64, 8, 4, 128, 200, 200, 0, 3),     # many units: single-split plan (direct)
+    (2, 9, 1, 128, 3000, 3000, 0, 0),    # two head chunks
+    (32, 12, 2, 128, 4096, 4096, 0, 2),  # the decode workload's shape, mixed lengths
+]
+
+
+def _varlen_inputs(case, seed):
+    b, hq, hkv, d, ms, bound, win, idle = case
+    w = synth.DecodeWorkload("varlen", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, window=win, seed=seed)
+    q, k, v = synth.decode_inputs(w)
+    lens = synth.seq_lengths(b, bound, seed=seed + 7, idle=idle)
+    return w, q, k, v, lens
+
+
+def _vmax_varlen(w, v, lens, plus=0):
+    vm = 0.0
+    for i, t in enumerate(lens):
+        t = int(t) + plus
+        if t:
+            lo = t - w.window if (w.window and t > w.window) else 0
+            vm = max(vm, float(np.abs(v[i, :, lo:t]).max()))
+    return vm
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES,
+                         ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_bd{}_w{}_idle{}".format(*c))
+def test_decode_varlen_matches_oracle(dev, case):
+    w, q, k, v, lens = _varlen_inputs(case, seed=sum(case) % 883)
+    b, hq, hkv, d, ms, bound, win, _ = case
+    out = torch.full((b, hq, d), float("nan"), device=dev)
+    ws = torch.full((A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win),), 0xFF,
+                    dtype=torch.uint8, device=dev)
+    A.attn_decode_varlen(torch.from_numpy(q).to(dev), torch.from_numpy(k).to(dev),
+                         torch.from_numpy(v).to(dev), out,
+                         torch.from_numpy(lens.astype(np.int32)).to(dev), b, hq, hkv, d, ms,
+                         bound, win, w.scale, ws)
+    torch.cuda.synchronize()
+    ref = oracle.decode_varlen(q, k, v, lens, b, hq, hkv, d, ms, win, w.scale)
+    got = out.cpu().numpy()
+    assert np.all(got[lens == 0] == 0.0)
+    _assert_close(got, ref, _vmax_varlen(w, v, lens), str(case))
+
+
+def test_decode_varlen_invalid_length_gives_nan_rows(dev):
+    """A length past seq_bound yields NaN for that sequence only."""
+    b, hq, hkv, d, ms, bound = 4, 12, 2, 128, 64, 40
+    w = synth.DecodeWorkload("varlen", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, seed=21)
+    q, k, v = synth.decode_inputs(w)
+    lens = np.array([40, 41, 0, 17], np.uint32)
+    out = torch.zeros((b, hq, d), device=dev)
+    ws = A.decode_workspace(b, hq, hkv, d, bound, 0)
+    A.attn_decode_varlen(torch.from_numpy(q).to(dev), torch.from_numpy(k).to(dev),
+                         torch.from_numpy(v).to(dev), out,
+                         torch.from_numpy(lens.astype(np.int32)).to(dev), b, hq, hkv, d, ms,
+                         bound, 0, w.scale, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[1])) and np.all(got[2] == 0.0)
+    ok = lens.copy()
+    ok[1] = 0
+    ref = oracle.decode_varlen(q, k, v, ok, b, hq, hkv, d, ms, 0, w.scale)
+    _assert_close(got[[0, 3]], ref[[0, 3]], _vmax_varlen(w, v, ok), "valid rows")
+
+
+VARLEN_APPEND_CASES = [
+    # (batch, hq, hkv, d, max_seq, bound, window)
+    (6, 12, 2, 128, 300, 300, 0),
+    (5, 4, 2, 64, 90, 90, 17),
+    (4, 8, 8, 32, 40, 1, 0),             # bound 1: every sequence at position 0
+    (64, 8, 4, 128, 200, 160, 0),
+    (32, 12, 2, 128, 4096, 4096, 0),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_APPEND_CASES,
+                         ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_bd{}_w{}".format(*c))
+def test_decode_append_varlen_matches_oracle(dev, case):
+    b, hq, hkv, d, ms, bound, win = case
+    seed = sum(case) % 877
+    w = synth.DecodeWorkload("varlen", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, window=win, seed=seed)
+    q, k, v = synth.decode_inputs(w)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=seed + 1)
+    pos = synth.seq_lengths(b, bound, seed=seed + 2) - 1        # positions in [0, bound)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    out = torch.full((b, hq, d), float("nan"), device=dev)
+    nws = A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win)
+    ws = torch.full((max(1, nws),), 0xFF, dtype=torch.uint8, device=dev)
+    A.attn_decode_append_varlen(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
+                                torch.from_numpy(vn).to(dev), kd, vd, out,
+                                torch.from_numpy(pos.astype(np.int32)).to(dev), b, hq, hkv, d,
+                                ms, bound, win, w.scale, ws)
+    torch.cuda.synchronize()
+    for i in range(b):   # the reference step: each sequence appends at its position
+        oracle.kv_append(kn[i:i + 1], vn[i:i + 1], k[i:i + 1], v[i:i + 1], 1, hkv, d, ms,
+                         int(pos[i]))
+    assert np.array_equal(kd.cpu().numpy(), k) and np.array_equal(vd.cpu().numpy(), v)
+    ref = oracle.decode_varlen(q, k, v, pos + 1, b, hq, hkv, d, ms, win, w.scale)
+    _assert_close(out.cpu().numpy(), ref, _vmax_varlen(w, v, pos, plus=1), str(case))
+
+
+def test_decode_append_varlen_invalid_position_and_no_heads(dev):
+    """positions[b] + 1 > seq_bound: NaN output, no write for that sequence;
+    num_heads == 0: the per-sequence appends alone."""
+    b, hq, hkv, d, ms, bound = 3, 6, 2, 64, 32, 20
+    w = synth.DecodeWorkload("varlen", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, seed=23)
+    q, k, v = synth.decode_inputs(w)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=24)
+    pos = np.array([19, 20, 4], np.uint32)
+    for heads in (hq, 0):
+        kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+        out = torch.zeros((b, max(heads, 1), d), device=dev)
+        ws = A.decode_workspace(b, hq, hkv, d, bound, 0)
+        A.attn_decode_append_varlen(torch.from_numpy(q).to(dev) if heads else 0,
+                                    torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev),
+                                    kd, vd, out if heads else 0,
+                                    torch.from_numpy(pos.astype(np.int32)).to(dev), b, heads,
+                                    hkv, d, ms, bound, 0, w.scale, ws if heads else None)
+        torch.cuda.synchronize()
+        kr, vr = k.copy(), v.copy()
+        for i in (0, 2):
+            oracle.kv_append(kn[i:i + 1], vn[i:i + 1], kr[i:i + 1], vr[i:i + 1], 1, hkv, d, ms,
+                             int(pos[i]))
+        assert np.array_equal(kd.cpu().numpy(), kr) and np.array_equal(vd.cpu().numpy(), vr)
+        if heads:
+            got = out.cpu().numpy()
+            assert np.all(np.isnan(got[1]))
+            ref = oracle.decode_varlen(q, kr, vr, np.where(pos < bound, pos + 1, 0), b, hq, hkv,
+                                       d, ms, 0, w.scale)
+            _assert_close(got[[0, 2]], ref[[0, 2]], _vmax_varlen(w, vr, pos[[0, 2]], plus=1),
+                          "valid rows")
+
+
 # ----------------------------------------------------------------- prefill
 
 def _gpu_prefill(dev, w, q, k, v, fill=float("nan")):
