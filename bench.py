@@ -251,7 +251,8 @@ def bench_decode_window(args, dev):
     return {"workload": w.name, "median_us": round(med * 1e3, 2),
             "min_us": round(min(ms) * 1e3, 2), "GB/s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("attn_decode_window")},
             "algorithmic_bytes": w.kv_bytes()}
 
 
@@ -323,7 +324,8 @@ def bench_decode_varlen(args, dev):
             "median_us": round(med * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
             "GB/s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("attn_decode_append_varlen")},
             "algorithmic_bytes": bytes_}
 
 
@@ -354,7 +356,8 @@ def bench_append_rows(args, dev):
     return {"workload": "append_rows_m16384_hkv8_d128", "median_us": round(med * 1e3, 2),
             "min_us": round(min(ms) * 1e3, 2), "GB/s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("kv_append_rows")},
             "algorithmic_bytes": bytes_}
 
 
