@@ -105,9 +105,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     static_assert(VPL % 4 == 0 && LPR * VPL == D, "lane tiling");
 
     __shared__ float s_acc[NSLOT][HC][D];  // per row slot partial accumulators
-    __shared__ float s_m[NSLOT][HC];
     __shared__ float s_l[NSLOT][HC];
-    __shared__ float s_f[NSLOT][HC];       // slot weight 2^(m_slot - M)
+    __shared__ float s_wm[NW][HC];         // per wave maximum reference
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -165,6 +164,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
 
     if (ntile > 0) {
+        // ring of P row steps in flight, issued first so that the q loads
+        // below wait under them; rows past rb are clamped to rb - 1 (in
+        // bounds, masked out of the softmax)
+        float4 kf[P][NF4], vf[P][NF4];
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            if (s > 0 && s >= (int)ntile) break;  // a ring slot no step uses: no load
+            const size_t off = (size_t)min(ra + s * kStride + r, rb - 1) * D;
+#pragma unroll
+            for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+#pragma unroll
+            for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+        }
+
         // q of every head of the chunk, pre-scaled (zero for heads past nh;
         // those re-read the last valid head so the load stays in bounds)
         float4 qv[HC][NF4];
@@ -221,17 +234,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         };
 
         {
-            // ring of P row steps in flight; rows past rb are clamped to rb - 1
-            // (in bounds, masked out of the softmax)
-            float4 kf[P][NF4], vf[P][NF4];
-#pragma unroll
-            for (int s = 0; s < P; ++s) {
-                const size_t off = (size_t)min(ra + s * kStride + r, rb - 1) * D;
-#pragma unroll
-                for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
-#pragma unroll
-                for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
-            }
             // reference m from the first step's scores
             {
                 const float pen = ra + r < rb ? 0.f : kNegInf;
@@ -246,17 +248,40 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int hh = 0; hh < HC; ++hh) m[hh] = fmaxf(sc[hh], kMinRef);
             }
-            for (uint32_t base = 0; base < ntile; base += P) {
+            // Steady state: groups of P steps, each refilling its ring slot
+            // with the step P ahead. The last P steps load nothing: a load no
+            // step consumes would still hold its registers, and the first
+            // reuse of them after the loop would wait for its HBM round trip.
+            const uint32_t nref = ntile > (uint32_t)P ? ntile - P : 0;  // steps that refill
+            uint32_t base = 0;
+            for (; base + P <= nref; base += P) {
 #pragma unroll
                 for (int s = 0; s < P; ++s) {
                     const uint32_t row = ra + (base + s) * kStride + r;
                     step(kf[s], vf[s], row);
-                    // refill this ring slot with the step P ahead
                     const size_t off = (size_t)min(row + P * kStride, rb - 1) * D;
 #pragma unroll
                     for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
 #pragma unroll
                     for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+                }
+            }
+            // tail: the remaining (fewer than 2P) steps, refilling only while a
+            // step P ahead exists (uniform branches)
+#pragma unroll
+            for (int s = 0; s < 2 * P - 1; ++s) {
+                if (base + s < ntile) {
+                    const uint32_t row = ra + (base + s) * kStride + r;
+                    step(kf[s % P], vf[s % P], row);
+                    if (base + s + P < ntile) {
+                        const size_t off = (size_t)min(row + P * kStride, rb - 1) * D;
+#pragma unroll
+                        for (int t = 0; t < NF4; ++t)
+                            kf[s % P][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+#pragma unroll
+                        for (int t = 0; t < NF4; ++t)
+                            vf[s % P][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+                    }
                 }
             }
         }
@@ -286,26 +311,37 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
     }
 
-    // every row slot of the workgroup lands in LDS
+    // The row slots merge against the workgroup's per-head maximum reference
+    // M: the maximum over a wave's slots comes from lane shuffles, over the
+    // waves from LDS; each slot then scales its own state by 2^(m - M)
+    // before it lands in LDS, so the final sum is a plain one.
+    {
+        float x[HC];
 #pragma unroll
-    for (int hh = 0; hh < HC; ++hh) {
+        for (int hh = 0; hh < HC; ++hh) x[hh] = m[hh];
 #pragma unroll
-        for (int t = 0; t < NF4; ++t) st4(&s_acc[slot][hh][4 * (c + LPR * t)], acc[hh][t]);
-        if (c == 0) {
-            s_m[slot][hh] = m[hh];
-            s_l[slot][hh] = l[hh];
+        for (int o = LPR; o < 64; o <<= 1) {  // stage-major: one round trip per stage
+            float y[HC];
+#pragma unroll
+            for (int hh = 0; hh < HC; ++hh) y[hh] = __shfl_xor(x[hh], o);
+#pragma unroll
+            for (int hh = 0; hh < HC; ++hh) x[hh] = fmaxf(x[hh], y[hh]);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int hh = 0; hh < HC; ++hh) s_wm[wave][hh] = x[hh];
         }
     }
     __syncthreads();
-    // slot weights against the workgroup max
-    if (tid < HC) {
-        float M = kNegInf;
-        for (int sl = 0; sl < NSLOT; ++sl) M = fmaxf(M, s_m[sl][tid]);
-        for (int sl = 0; sl < NSLOT; ++sl) {
-            const float ms = s_m[sl][tid];
-            s_f[sl][tid] = ms == kNegInf ? 0.f : fast_exp2(ms - M);
-        }
-        s_m[0][tid] = M;  // slot 0's m is no longer needed
+#pragma unroll
+    for (int hh = 0; hh < HC; ++hh) {
+        float M = s_wm[0][hh];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) M = fmaxf(M, s_wm[w2][hh]);
+        const float f = fast_exp2(m[hh] - M);  // m, M >= kMinRef: finite, no NaN
+#pragma unroll
+        for (int t = 0; t < NF4; ++t) st4(&s_acc[slot][hh][4 * (c + LPR * t)], acc[hh][t] * f);
+        if (c == 0) s_l[slot][hh] = l[hh] * f;
     }
     __syncthreads();
 
@@ -316,10 +352,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         const int d = idx % D;
         float x = 0.f;
 #pragma unroll 8
-        for (int sl = 0; sl < NSLOT; ++sl) x += s_acc[sl][hh][d] * s_f[sl][hh];
+        for (int sl = 0; sl < NSLOT; ++sl) x += s_acc[sl][hh][d];
         float lsum = 0.f;
         if (d == 0 || MERGE == kMergeDirect)
-            for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh] * s_f[sl][hh];
+            for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh];
         if constexpr (MERGE == kMergeDirect) {
             // no rows (an idle sequence): 0; an invalid length: NaN
             const float o = !sr.valid ? __builtin_nanf("") : lsum > 0.f ? x / lsum : 0.f;
@@ -327,7 +363,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         } else {
             mypart[hh * (D + 2) + d] = x;
             if (d == 0) {
-                mypart[hh * (D + 2) + D] = s_m[0][hh];
+                float M = s_wm[0][hh];
+                for (int w2 = 1; w2 < NW; ++w2) M = fmaxf(M, s_wm[w2][hh]);
+                mypart[hh * (D + 2) + D] = M;
                 mypart[hh * (D + 2) + D + 1] = lsum;
             }
         }
@@ -386,7 +424,36 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     constexpr uint32_t SS = HC * (D + 2);  // floats between splits
     const float *up = a.part + (size_t)unit * a.n_split * SS + hh * (D + 2);
 
+    // partial states are read eight splits per round (independent loads);
+    // a round's entries past ns re-read the last split with weight 0
+    float ms[8], ls[8], xs[8];
+    auto load_round = [&](uint32_t s0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t sp = min(s0 + i, ns - 1);
+            const float *ps = up + (size_t)sp * SS;
+            ms[i] = s0 + i < ns ? ps[D] : kNegInf;
+            ls[i] = ps[D + 1];
+            xs[i] = ps[tid];
+        }
+    };
     float M = kNegInf, num = 0.f, den = 0.f;
+    auto fold_round = [&]() {
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Mn = fmaxf(Mn, ms[i]);
+        const float c = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+        num *= c;
+        den *= c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = ms[i] == kNegInf ? 0.f : fast_exp2(ms[i] - Mn);
+            num += xs[i] * w;
+            den += ls[i] * w;
+        }
+        M = Mn;
+    };
+    if (ns > 0) load_round(0);  // in flight while the new row is scored
     if (a.k_new != nullptr) {
         const float *knp = a.k_new + (size_t)bg * D;
         const float *qp = a.q + ((size_t)b * a.num_heads + h) * D;
@@ -410,29 +477,10 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
             a.v_dst[dst] = vn;
         }
     }
-    for (uint32_t s0 = 0; s0 < ns; s0 += 8) {
-        float ms[8], ls[8], xs[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t sp = min(s0 + i, ns - 1);  // past the end: re-read, weight 0
-            const float *ps = up + (size_t)sp * SS;
-            ms[i] = s0 + i < ns ? ps[D] : kNegInf;
-            ls[i] = ps[D + 1];
-            xs[i] = ps[tid];
-        }
-        float Mn = M;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) Mn = fmaxf(Mn, ms[i]);
-        const float c = M == kNegInf ? 0.f : fast_exp2(M - Mn);
-        num *= c;
-        den *= c;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float w = ms[i] == kNegInf ? 0.f : fast_exp2(ms[i] - Mn);
-            num += xs[i] * w;
-            den += ls[i] * w;
-        }
-        M = Mn;
+    if (ns > 0) fold_round();
+    for (uint32_t s0 = 8; s0 < ns; s0 += 8) {
+        load_round(s0);
+        fold_round();
     }
     // den is 0 only for an idle sequence (no rows, nothing appended)
     a.out[((size_t)b * a.num_heads + h) * D + tid] = den > 0.f ? num / den : 0.f;
