@@ -57,12 +57,15 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads, uint32_t 
     if (batch == 0 || num_heads == 0) return 0;
     if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return 0;
     // large enough for every decode entry point's plan of these shapes
-    const size_t a =
-        attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window).workspace_bytes;
-    const size_t b = attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window,
-                                       false, true)
-                         .workspace_bytes;
-    return a > b ? a : b;
+    size_t need = 0;
+    for (int append = 0; append < 2; ++append)
+        for (int varlen = 0; varlen < 2; ++varlen) {
+            const size_t n = attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq,
+                                               window, append != 0, varlen != 0)
+                                 .workspace_bytes;
+            need = n > need ? n : need;
+        }
+    return need;
 }
 
 attn_status attn_decode(const float *q, const float *k_cache, const float *v_cache, float *out,

@@ -8,13 +8,15 @@ namespace {
 constexpr int kDecodeWaves = 4;          // waves per workgroup
 constexpr int kPrefetch = 2;             // row steps in flight per wave
 constexpr int kTargetWorkgroups = 256;   // one workgroup per CU, streaming long ranges
-// Per-sequence lengths are only known on the device: the plan is made for the
-// bound, and splits past a shorter sequence's end exit at once. Shorter splits
-// (two workgroups per CU for a batch at the bound) keep more rows in flight
-// when many splits are empty; measured on a 32-sequence batch, 4096-row
-// bound: lengths uniform in [1, 4096] 47 -> 40 us, every length 4096
-// 49 -> 52 us, against the single-length target.
-constexpr int kTargetWorkgroupsVarlen = 512;
+// Per-sequence lengths are only known on the device: each workgroup of the
+// split pass evaluates the proportional table (a unit's share of the splits
+// follows its rows, so every split holds about the same number of rows).
+// The split counts are rounded up per unit, which adds about units / 2
+// splits: the target leaves room for them, so the splits holding rows still
+// fit one workgroup per CU.
+constexpr uint32_t kTargetWorkgroupsVarlen(uint32_t units) {
+    return units / 2 + 64 < (uint32_t)kTargetWorkgroups ? kTargetWorkgroups - units / 2 : 64;
+}
 constexpr int kMinRowsPerWave = 32;
 
 constexpr int lanes_per_row(int d) { return d == 32 ? 8 : 16; }
@@ -24,8 +26,7 @@ constexpr int lanes_per_row(int d) { return d == 32 ? 8 : 16; }
 // a single split per unit and no appended row, pass 1 writes the normalised
 // output itself.
 template <int D, int HC>
-hipError_t launch_hc(const DecodeArgs &args, uint32_t units, uint32_t n_split,
-                     hipStream_t stream) {
+hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStream_t stream) {
     constexpr int LPR = lanes_per_row(D);
     if (n_split == 1 && args.k_new == nullptr) {
         hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeDirect,
@@ -33,10 +34,20 @@ hipError_t launch_hc(const DecodeArgs &args, uint32_t units, uint32_t n_split,
                            dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
         return hipGetLastError();
     }
+    uint32_t grid = units * n_split;
+    if (args.lens != nullptr) {
+        // proportional splits: at most g_target + units of them hold rows;
+        // the workgroups past the last one exit at once
+        args.units = units;
+        args.g_target = kTargetWorkgroupsVarlen(units);
+        args.min_rows = kDecodeWaves * kMinRowsPerWave;
+        args.rows_step = kDecodeWaves * (64 / LPR);
+        grid = args.g_target + units;
+    }
     if (n_split > 0) {
         hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch,
                                           kMergePartialOnly, true, true>),
-                           dim3(units * n_split), dim3(kDecodeWaves * 64), 0, stream, args);
+                           dim3(grid), dim3(kDecodeWaves * 64), 0, stream, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -85,7 +96,7 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     const uint32_t rpt = 64 / lanes_per_row((int)head_dim);
     const uint32_t step = kDecodeWaves * rpt;
     const uint32_t max_split = ceil_div(len, (uint64_t)kDecodeWaves * kMinRowsPerWave);
-    uint32_t n_split = ceil_div(varlen ? kTargetWorkgroupsVarlen : kTargetWorkgroups, p.units);
+    uint32_t n_split = ceil_div(kTargetWorkgroups, p.units);
     n_split = n_split > max_split ? max_split : n_split;
     n_split = n_split > (uint32_t)kMaxSplit ? (uint32_t)kMaxSplit : n_split;
     n_split = n_split < 1 ? 1 : n_split;
@@ -93,7 +104,13 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     rows = ceil_div(rows, step) * step;
     p.rows_per_split = rows;
     p.n_split = ceil_div(len, rows);
-    p.part_floats = (size_t)p.units * p.n_split * p.head_chunk * (head_dim + 2);
+    // per-sequence lengths: the proportional table has at most
+    // target + units splits (the split pass runs unless the plan has a
+    // single split and no appended row)
+    const size_t slots = varlen && !(p.n_split == 1 && !append)
+                             ? (size_t)kTargetWorkgroupsVarlen(p.units) + p.units
+                             : (size_t)p.units * p.n_split;
+    p.part_floats = slots * p.head_chunk * (head_dim + 2);
     p.workspace_bytes = p.part_floats * sizeof(float);
     return p;
 }

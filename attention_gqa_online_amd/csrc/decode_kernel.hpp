@@ -64,6 +64,9 @@ struct DecodeArgs {
     // append (len_add = 1, lens = positions) the new row is row T_b - 1
     const uint32_t *lens;
     uint32_t len_add, seq_bound, window;
+    // with per-sequence lengths the split pass gives each unit a share of
+    // g_target workgroups in proportion to its rows (prop_split)
+    uint32_t units, g_target, min_rows, rows_step;
     uint32_t num_heads, kv_heads, hpk, n_chunks, max_seq;
     uint32_t w0, total_seq, n_split, rows_per_split;
     float qscale;     // scale * log2(e): scores come out in log2 units
@@ -84,6 +87,86 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, uint32_t b) {
     const uint32_t T = valid ? (uint32_t)t : 0;
     const uint32_t w0 = (a.window > 0 && T > a.window) ? T - a.window : 0;
     return {w0, T > 0 ? T - a.len_add : 0, T > 0 ? T - 1 : 0, valid};
+}
+
+// Rows of the split pass of unit u (per-sequence lengths).
+__device__ __forceinline__ uint32_t unit_rows(const DecodeArgs &a, uint32_t u) {
+    const SeqRange r = seq_range(a, (u / a.n_chunks) / a.kv_heads);
+    return r.hi > r.w0 ? r.hi - r.w0 : 0;
+}
+
+// Split of a unit with L of the batch's T rows: n splits of `rows` rows, n
+// about L * g_target / T (at least 1, at most one per min_rows rows), rows a
+// multiple of rows_step. Both passes evaluate it identically.
+struct PropSplit {
+    uint32_t n, rows;
+};
+
+__device__ __forceinline__ PropSplit prop_split(const DecodeArgs &a, uint32_t L, uint64_t T) {
+    if (L == 0) return {0, 0};
+    const uint64_t want = ((uint64_t)L * a.g_target + T - 1) / T;
+    const uint64_t cap = ((uint64_t)L + a.min_rows - 1) / a.min_rows;
+    const uint32_t n0 = (uint32_t)(want < cap ? want : cap);
+    uint32_t rows = (L + n0 - 1) / n0;
+    rows = (rows + a.rows_step - 1) / a.rows_step * a.rows_step;
+    return {(L + rows - 1) / rows, rows};
+}
+
+// The proportional split table is evaluated by each wave on its own (the
+// waves of a workgroup compute it redundantly: no LDS, no barrier), over W
+// active lanes (64, or 32 for a 32-thread workgroup). Lane l takes units
+// l, l + W, ...; splits are numbered unit by unit.
+template <int W>
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, W);
+    return x;
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, W);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// The batch's rows of the split pass.
+template <int W>
+__device__ __forceinline__ uint64_t prop_total(const DecodeArgs &a, int lane) {
+    uint64_t t = 0;
+    for (uint32_t u = lane; u < a.units; u += W) t += unit_rows(a, u);
+    return wave_sum_u64<W>(t);
+}
+
+struct PropHit {
+    uint32_t unit, first, n, rows;
+    bool found;
+};
+
+// The unit holding split index w (by_unit = false), or unit w itself
+// (by_unit = true); first = its first split index, n its split count.
+template <int W>
+__device__ __forceinline__ PropHit prop_find(const DecodeArgs &a, uint64_t T, uint32_t w,
+                                             bool by_unit, int lane) {
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < a.units; base += W) {
+        const uint32_t u = base + lane;
+        const PropSplit ps = u < a.units ? prop_split(a, unit_rows(a, u), T) : PropSplit{0, 0};
+        const uint32_t incl = wave_incl_scan<W>(ps.n, lane);
+        const uint32_t S = carry + incl - ps.n;
+        const bool hit = by_unit ? u == w : (ps.n != 0 && S <= w && w - S < ps.n);
+        const unsigned long long mask = __ballot(hit);
+        if (mask != 0) {
+            const int src = __ffsll((long long)mask) - 1;
+            return {(uint32_t)__shfl((int)u, src), (uint32_t)__shfl((int)S, src),
+                    (uint32_t)__shfl((int)ps.n, src), (uint32_t)__shfl((int)ps.rows, src), true};
+        }
+        carry += (uint32_t)__shfl((int)incl, W - 1);
+    }
+    return {0, 0, 0, 0, false};
 }
 
 template <bool NT>
@@ -115,8 +198,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int c = lane % LPR;
     const int slot = wave * RPT + r;
 
-    const uint32_t split = blockIdx.x % a.n_split;
-    const uint32_t unit = blockIdx.x / a.n_split;
+    uint32_t split = blockIdx.x % a.n_split;
+    uint32_t unit = blockIdx.x / a.n_split;
+    uint32_t rps = a.rows_per_split;
+    if constexpr (MERGE == kMergePartialOnly) {
+        if (a.lens != nullptr) {
+            // per-sequence lengths: workgroup w is split w - first(u) of the
+            // unit u whose splits include w (proportional table)
+            const uint64_t T = prop_total<64>(a, lane);
+            const PropHit ph = prop_find<64>(a, T, blockIdx.x, false, lane);
+            if (!ph.found) return;  // past the last split (uniform)
+            unit = ph.unit;
+            split = blockIdx.x - ph.first;
+            rps = ph.rows;
+        }
+    }
     const uint32_t chunk = unit % a.n_chunks;
     const uint32_t bg = unit / a.n_chunks;  // b * kv_heads + g
     const uint32_t g = bg % a.kv_heads;
@@ -128,14 +224,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     // rows of this workgroup, then of this wave: either a contiguous quarter
     // of the workgroup's range, or every NW-th step of it (INTERLEAVE)
     const SeqRange sr = seq_range(a, b);
-    const uint32_t ws0 = sr.w0 + split * a.rows_per_split;
-    const uint32_t ws1 = min(ws0 + a.rows_per_split, sr.hi);
-    if constexpr (MERGE == kMergePartialOnly) {
-        // a split past a shorter sequence's end: nothing to write, the merge
-        // pass folds only the splits that hold rows (uniform per workgroup)
-        if (a.lens != nullptr && ws0 >= ws1) return;
-    }
-    const uint32_t per_wave = a.rows_per_split / NW;
+    const uint32_t ws0 = sr.w0 + split * rps;
+    const uint32_t ws1 = min(ws0 + rps, sr.hi);
+    const uint32_t per_wave = rps / NW;
     const uint32_t ra = INTERLEAVE ? ws0 + wave * RPT : min(ws0 + wave * per_wave, ws1);
     const uint32_t rb = INTERLEAVE ? ws1 : min(ra + per_wave, ws1);
     constexpr uint32_t kStride = INTERLEAVE ? NW * RPT : RPT;  // rows between a wave's steps
@@ -346,7 +437,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     __syncthreads();
 
     // this workgroup's partial state per head: (acc[d], M, L)
-    float *mypart = a.part + ((size_t)unit * a.n_split + split) * HC * (D + 2);
+    float *mypart = a.part + (size_t)blockIdx.x * HC * (D + 2);  // split index = workgroup
     for (int idx = tid; idx < HC * D; idx += NW * 64) {
         const int hh = idx / D;
         const int d = idx % D;
@@ -412,17 +503,22 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     const uint32_t h = g * a.hpk + hl0 + hh;
     const SeqRange sr = seq_range(a, b);
     uint32_t ns = a.n_split;
+    size_t first = (size_t)unit * a.n_split;  // the unit's first split index
     if (a.lens != nullptr) {
         if (!sr.valid) {  // invalid length: NaN output, nothing appended
             a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
             return;
         }
-        // only the splits that start before this sequence's end hold rows
-        const uint32_t rows = sr.hi > sr.w0 ? sr.hi - sr.w0 : 0;
-        ns = ns == 0 ? 0 : (rows + a.rows_per_split - 1) / a.rows_per_split;
+        if (ns != 0) {  // the split pass ran with the proportional table
+            constexpr int W = D < 64 ? D : 64;
+            const int lane = tid & 63;
+            const PropHit ph = prop_find<W>(a, prop_total<W>(a, lane), unit, true, lane);
+            first = ph.first;
+            ns = ph.n;
+        }
     }
     constexpr uint32_t SS = HC * (D + 2);  // floats between splits
-    const float *up = a.part + (size_t)unit * a.n_split * SS + hh * (D + 2);
+    const float *up = a.part + first * SS + hh * (D + 2);
 
     // partial states are read eight splits per round (independent loads);
     // a round's entries past ns re-read the last split with weight 0
