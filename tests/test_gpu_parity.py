@@ -824,3 +824,89 @@ def test_decode_calls_replay_correctly_from_a_hip_graph(dev):
     oracle.kv_append(kn, vn, k, v, b, hkv, d, ms, pos)
     _assert_close(out_e.cpu().numpy(), _ref_decode(w.with_(total_seq=pos + 1), q, k, v),
                   _vmax_decode(w, v), "graph case eager")
+
+
+def test_varlen_decode_step_graph_follows_device_positions(dev):
+    """A decode step of a mixed-length batch captured once in a HIP graph
+    serves new positions and new rows on every replay: the positions live in
+    device memory and are rewritten between replays (with other eager work),
+    and each replay matches the oracle's append + decode at those positions."""
+    b, hq, hkv, d, ms = 3, 12, 2, 128, 600
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, ms, seed=41)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    knd = torch.empty(b, hkv, d, device=dev)
+    vnd = torch.empty(b, hkv, d, device=dev)
+    pos_d = torch.zeros(b, dtype=torch.int32, device=dev)
+    out = torch.empty(b, hq, d, device=dev)
+    ws = A.decode_workspace(b, hq, hkv, d, ms, 0, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.attn_decode_append_varlen(qd, knd, vnd, kd, vd, out, pos_d, b, hq, hkv, d, ms, ms, 0,
+                                    w.scale, ws)
+    kr, vr = k.copy(), v.copy()   # host mirror of the caches
+    for rep, pos in enumerate([[100, 5, 599], [101, 0, 300], [37, 6, 598]]):
+        pos = np.array(pos, np.uint32)
+        kn, vn = synth.append_inputs(b, hkv, d, seed=50 + rep)
+        knd.copy_(torch.from_numpy(kn))
+        vnd.copy_(torch.from_numpy(vn))
+        pos_d.copy_(torch.from_numpy(pos.astype(np.int32)))
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(b):
+            oracle.kv_append(kn[i:i + 1], vn[i:i + 1], kr[i:i + 1], vr[i:i + 1], 1, hkv, d, ms,
+                             int(pos[i]))
+        assert np.array_equal(kd.cpu().numpy(), kr) and np.array_equal(vd.cpu().numpy(), vr)
+        ref = oracle.decode_varlen(q, kr, vr, pos + 1, b, hq, hkv, d, ms, 0, w.scale)
+        vmax = max(float(np.abs(vr[i, :, :pos[i] + 1]).max()) for i in range(b))
+        _assert_close(out.cpu().numpy(), ref, vmax, f"replay {rep}")
+        assert bool(torch.isfinite(junk))
+
+
+def test_serving_calls_replay_from_a_hip_graph(dev):
+    """Prefill, bulk append and the rotary decode step captured in one HIP
+    graph: every replay gives the eager results bit for bit."""
+    m, hq, hpk, d, ms = 200, 12, 6, 128, 256
+    hkv = hq // hpk
+    w = synth.PrefillWorkload("g", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d, kv_stride=hkv * d, seed=61)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in synth.prefill_inputs(w))
+    qn = torch.randn(1, hq, d, device=dev)
+    kn = torch.randn(1, hkv, d, device=dev)
+    vn = torch.randn(1, hkv, d, device=dev)
+    cos_t, sin_t = (torch.from_numpy(x).to(dev) for x in synth.rope_tables(d, m))
+    ws = A.decode_workspace(1, hq, hkv, d, m + 1, 0, device=dev)
+
+    def run(o, kc, vc, out):
+        A.attn_prefill_causal(q, k, v, o, m, hq * d, hkv * d, hq, hpk, d)
+        A.kv_append_rows(k, v, kc, vc, m, hkv * d, hkv, d, ms, 0)
+        A.attn_decode_rope_append(qn, kn, vn, cos_t, sin_t, kc, vc, out, 1, hq, hkv, d, ms, m,
+                                  0, 0.08838835, ws)
+
+    def fresh():
+        return (torch.full((m, hq * d), float("nan"), device=dev),
+                torch.full((1, hkv, ms, d), float("nan"), device=dev),
+                torch.full((1, hkv, ms, d), float("nan"), device=dev),
+                torch.full((1, hq, d), float("nan"), device=dev))
+    eager = fresh()
+    run(*eager)
+    torch.cuda.synchronize()
+    graph_bufs = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(*graph_bufs)
+    for rep in range(3):
+        for t in graph_bufs:
+            t.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        for a_, b_ in zip(eager[:1] + eager[3:], graph_bufs[:1] + graph_bufs[3:]):
+            assert torch.equal(a_, b_), f"replay {rep}"
+        # cache rows 0..m are written (m by the decode step); the rest stay NaN
+        for a_, b_ in zip(eager[1:3], graph_bufs[1:3]):
+            assert torch.equal(a_[:, :, :m + 1], b_[:, :, :m + 1]), f"replay {rep}"
+            assert bool(torch.isnan(b_[:, :, m + 1:]).all())
+        assert bool(torch.isfinite(junk))
+    assert bool(torch.isfinite(eager[3]).all())
