@@ -910,3 +910,47 @@ def test_serving_calls_replay_from_a_hip_graph(dev):
             assert bool(torch.isnan(b_[:, :, m + 1:]).all())
         assert bool(torch.isfinite(junk))
     assert bool(torch.isfinite(eager[3]).all())
+
+
+# ------------------------------------------------------------- large offsets
+
+def test_decode_one_sequence_of_a_million_rows(dev):
+    """One sequence with 2^20 cached rows and 8 KV heads: 4 GiB per cache, so
+    byte offsets pass 2^32 (the caches are drawn on the GPU and copied back
+    for the oracle)."""
+    w = synth.DecodeWorkload("long", batch=1, num_heads=16, kv_heads=8, head_dim=128,
+                             max_seq=1 << 20, total_seq=1 << 20, seed=77)
+    q, k, v = synth.decode_inputs_device(w, 77, dev)
+    out = torch.full((1, 16, 128), float("nan"), device=dev)
+    ws = A.decode_workspace(1, 16, 8, 128, w.total_seq, 0, device=dev)
+    A.attn_decode(q, k, v, out, 1, 16, 8, 128, w.max_seq, w.total_seq, 0, w.scale, ws)
+    torch.cuda.synchronize()
+    qn, kn, vn = q.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    del k, v
+    torch.cuda.empty_cache()
+    ref = oracle.decode(qn, kn, vn, 1, 16, 8, 128, w.max_seq, w.total_seq, 0, w.scale)
+    _assert_close(out.cpu().numpy(), ref, float(np.abs(vn).max()), "2^20 rows")
+
+
+def test_prefill_past_two_gib_of_q(dev):
+    """m = 65536 rows of 64 query heads (Q and O 2 GiB each): byte offsets of
+    late rows pass 2^31. Sample: the last row of every head plus 256 seeded
+    (row, head) pairs from the second half."""
+    w = synth.PrefillWorkload("big", m=65536, num_q_heads=64, heads_per_kv=8, head_dim=128,
+                              q_stride=64 * 128, kv_stride=8 * 128, seed=65)
+    q, k, v = synth.prefill_inputs_device(w, 65, dev)
+    o = torch.full((w.m, w.q_stride), float("nan"), device=dev)
+    A.attn_prefill_causal(q, k, v, o, w.m, w.q_stride, w.kv_stride, 64, 8, 128)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(66)
+    rows = np.concatenate([np.full(64, w.m - 1), rng.integers(w.m // 2, w.m, 256)])
+    heads = np.concatenate([np.arange(64), rng.integers(0, 64, 256)])
+    got = o.view(w.m, 64, 128)[torch.from_numpy(rows).to(dev), torch.from_numpy(heads).to(dev)]
+    got = got.cpu().numpy()
+    del o
+    qn, kn, vn = q.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    del q, k, v
+    torch.cuda.empty_cache()
+    ref = oracle.prefill_causal(qn, kn, vn, w.m, w.q_stride, w.kv_stride, 64, 8, 128,
+                                rows=rows.astype(np.uint32), heads=heads.astype(np.uint32))
+    _assert_close(got, ref, float(np.abs(vn).max()), "m 65536")
