@@ -186,25 +186,51 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
             int xj = j;
             asm volatile("" : "+v"(xj));
 
-            // S^T = K_tile . Q^T, two 32-key blocks
+            // S^T = K_tile . Q^T, two 32-key blocks. The K operands of step
+            // u + 1 are read from LDS while the MFMAs of step u run (two
+            // register sets), so the matrix pipe does not wait on LDS.
             floatx16 s0, s1;
 #pragma unroll
             for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+            // chunk 2u + half of row j sits at (2u + half) ^ (j mod SW) =
+            // 2u ^ xh: one XOR with a constant per step, no per-step register
+            constexpr int SW = D / 4 < 16 ? D / 4 : 16;
+            int xh = (j & (SW - 1)) ^ half;
+            asm volatile("" : "+v"(xh));
+            const float *krow = sk + j * D;
+            // a wave in a matrix phase gets issue priority, so the SIMD's
+            // other wave fills the MFMA pipe's gaps with its vector work
+            __builtin_amdgcn_s_setprio(1);
+            float4 ka[2], kb[2];
+            ka[0] = ld4(krow + 4 * xh);
+            kb[0] = ld4(krow + 4 * xh + 32 * D);  // row 32 + j: same swizzle
 #pragma unroll
             for (int u = 0; u < NQ; ++u) {
-                const int c = 2 * u + half;
-                const float *kp = sk + j * D + 4 * swz_chunk<D>(xj, c);
-                const float4 ka = ld4(kp);
-                const float4 kb = ld4(kp + 32 * D);  // row 32 + j has the same swizzle
-                s0 = mfma32(ka.x, qt[u].x, s0);
-                s1 = mfma32(kb.x, qt[u].x, s1);
-                s0 = mfma32(ka.y, qt[u].y, s0);
-                s1 = mfma32(kb.y, qt[u].y, s1);
-                s0 = mfma32(ka.z, qt[u].z, s0);
-                s1 = mfma32(kb.z, qt[u].z, s1);
-                s0 = mfma32(ka.w, qt[u].w, s0);
-                s1 = mfma32(kb.w, qt[u].w, s1);
+                if (u + 1 < NQ) {
+                    const float *kp = krow + 4 * ((2 * (u + 1)) ^ xh);
+                    ka[(u + 1) & 1] = ld4(kp);
+                    kb[(u + 1) & 1] = ld4(kp + 32 * D);
+                }
+                const float4 a0 = ka[u & 1], b0 = kb[u & 1];
+                s0 = mfma32(a0.x, qt[u].x, s0);
+                s1 = mfma32(b0.x, qt[u].x, s1);
+                s0 = mfma32(a0.y, qt[u].y, s0);
+                s1 = mfma32(b0.y, qt[u].y, s1);
+                s0 = mfma32(a0.z, qt[u].z, s0);
+                s1 = mfma32(b0.z, qt[u].z, s1);
+                s0 = mfma32(a0.w, qt[u].w, s0);
+                s1 = mfma32(b0.w, qt[u].w, s1);
             }
+            // keep that order through scheduling: the reads of step u + 1
+            // go ahead of the 8 MFMAs of step u
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads of steps 0, 1
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMAs of step u
+                if (u + 2 < NQ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of u + 2
+            }
+
+            __builtin_amdgcn_s_setprio(0);
 
             // causal mask on tiles that reach past this wave's first row (also
             // removes the re-read rows past m: their keys exceed every query)
@@ -238,6 +264,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[md][e] *= cf;
 
+            __builtin_amdgcn_s_setprio(1);
             // O^T += V_tile^T . P^T; k-step (block mb, register e) uses key
             // 32mb + 8(e/4) + 4half + e%4, the key register e of S^T holds
 #pragma unroll
@@ -279,6 +306,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int md = 0; md < NMD; ++md) acc[md] = mfma32(vb[md], s1[e], acc[md]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
