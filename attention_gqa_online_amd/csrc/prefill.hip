@@ -47,6 +47,7 @@ constexpr int kWaves = 8;
 constexpr int kBr = 32;  // query rows per wave
 constexpr int kBc = 64;  // keys per LDS tile
 constexpr int kCus = 256;  // compute units of an MI355X
+constexpr float kLazyRescale = 8.0f;  // log2 units
 
 struct PrefillArgs {
     const float *q;
@@ -248,21 +249,30 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrow, mx);
-            const float cf = fast_exp2(mrow - mnew);
-            mrow = mnew;
+            // The reference max is raised (and O, l rescaled) only when some
+            // row of the wave sees a score more than kLazyRescale above it;
+            // otherwise the weights 2^(s - m) stay below 2^kLazyRescale and
+            // O / l is the same for any reference. Every processed tile has
+            // an unmasked key per row, so mx is finite; the first tile always
+            // raises m from -inf.
+            if (__any(mx > mrow + kLazyRescale)) {  // wave-uniform branch
+                const float mnew = fmaxf(mrow, mx);
+                const float cf = fast_exp2(mrow - mnew);
+                mrow = mnew;
+                lrow *= cf;
+#pragma unroll
+                for (int md = 0; md < NMD; ++md)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[md][e] *= cf;
+            }
             float ls = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                s0[e] = fast_exp2(s0[e] - mnew);
-                s1[e] = fast_exp2(s1[e] - mnew);
+                s0[e] = fast_exp2(s0[e] - mrow);
+                s1[e] = fast_exp2(s1[e] - mrow);
                 ls += s0[e] + s1[e];
             }
-            lrow = lrow * cf + ls;
-#pragma unroll
-            for (int md = 0; md < NMD; ++md)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[md][e] *= cf;
+            lrow += ls;
 
             __builtin_amdgcn_s_setprio(1);
             // O^T += V_tile^T . P^T; k-step (block mb, register e) uses key

@@ -954,3 +954,39 @@ def test_prefill_past_two_gib_of_q(dev):
     ref = oracle.prefill_causal(qn, kn, vn, w.m, w.q_stride, w.kv_stride, 64, 8, 128,
                                 rows=rows.astype(np.uint32), heads=heads.astype(np.uint32))
     _assert_close(got, ref, float(np.abs(vn).max()), "m 65536")
+
+
+@pytest.mark.parametrize("per_tile,m", [(6.0, 700), (9.0, 700), (25.0, 256)])
+def test_prefill_rising_scores(dev, per_tile, m):
+    """Scores that rise along the keys by `per_tile` log2 units per 64 keys
+    (below, just above and far above the point where the kernel raises its
+    reference maximum); the top score stays near 100 log2 units, where fp32
+    scores still meet the bar (a dot product of magnitude S carries a
+    rounding error of order S * 2^-24)."""
+    hq, hpk, d = 4, 2, 64
+    hkv = hq // hpk
+    rng = np.random.default_rng(int(per_tile * 10))
+    scale = 1.0 / np.sqrt(d)
+    q = np.zeros((m, hq * d), np.float32)
+    k = np.zeros((m, hkv * d), np.float32)
+    q[:, :] = (rng.standard_normal((m, hq * d)) * 0.1 + 1.0).astype(np.float32)
+    # score_j ~ scale * <q, k_j> * log2(e) = per_tile * j / 64 (+ noise)
+    slope = per_tile / 64.0 / (scale * np.log2(np.e) * d)
+    k[:, :] = (np.arange(m)[:, None] * slope
+               + rng.standard_normal((m, hkv * d)) * 0.05).astype(np.float32)
+    v = rng.standard_normal((m, hkv * d)).astype(np.float32)
+    w = synth.PrefillWorkload("rise", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d, kv_stride=hkv * d, seed=0)
+    o = _gpu_prefill(dev, w, q, k, v)
+    _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), float(np.abs(v).max()),
+                  f"rising {per_tile}")
+
+
+def test_prefill_wide_score_spread(dev):
+    """q and K with standard deviation 6: scores spread over hundreds of log2
+    units, most weights underflow, the reference maximum moves often."""
+    w = synth.PrefillWorkload("wide", m=900, num_q_heads=8, heads_per_kv=4, head_dim=128,
+                              q_stride=8 * 128, kv_stride=2 * 128, sigma=6.0, seed=901)
+    q, k, v = synth.prefill_inputs(w)
+    o = _gpu_prefill(dev, w, q, k, v)
+    _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), _vmax_prefill(w, v), "wide")
