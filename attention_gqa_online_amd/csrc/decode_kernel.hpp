@@ -169,17 +169,11 @@ __device__ __forceinline__ PropHit prop_find(const DecodeArgs &a, uint64_t T, ui
     return {0, 0, 0, 0, false};
 }
 
-template <bool NT>
-__device__ __forceinline__ float4 kv_load(const float *p) {
-    if constexpr (NT) return ld4_stream(p);
-    else return ld4(p);
-}
-
 // What the split pass writes: one partial state per (unit, split, head) for
 // the merge kernel, or, with a single split per unit, the normalised output.
 enum DecodeMerge { kMergePartialOnly = 1, kMergeDirect = 3 };
 
-template <int D, int HC, int LPR, int NW, int P, int MERGE, bool NT, bool INTERLEAVE>
+template <int D, int HC, int LPR, int NW, int P, int MERGE>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     constexpr int VPL = D / LPR;   // floats per lane per row
     constexpr int NF4 = VPL / 4;   // float4 per lane per row
@@ -221,15 +215,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int nh = min(HC, (int)(a.hpk - hl0));
     const uint32_t h0 = g * a.hpk + hl0;
 
-    // rows of this workgroup, then of this wave: either a contiguous quarter
-    // of the workgroup's range, or every NW-th step of it (INTERLEAVE)
+    // rows of this workgroup, then of this wave: every NW-th step of the
+    // workgroup's range, so the workgroup streams one contiguous region
     const SeqRange sr = seq_range(a, b);
     const uint32_t ws0 = sr.w0 + split * rps;
     const uint32_t ws1 = min(ws0 + rps, sr.hi);
-    const uint32_t per_wave = rps / NW;
-    const uint32_t ra = INTERLEAVE ? ws0 + wave * RPT : min(ws0 + wave * per_wave, ws1);
-    const uint32_t rb = INTERLEAVE ? ws1 : min(ra + per_wave, ws1);
-    constexpr uint32_t kStride = INTERLEAVE ? NW * RPT : RPT;  // rows between a wave's steps
+    const uint32_t ra = ws0 + wave * RPT;
+    const uint32_t rb = ws1;
+    constexpr uint32_t kStride = NW * RPT;  // rows between a wave's steps
     const uint32_t ntile = rb > ra ? (rb - ra + kStride - 1) / kStride : 0;
 
     const size_t cache_base = (size_t)bg * a.max_seq * D + 4 * c;
@@ -264,9 +257,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             if (s > 0 && s >= (int)ntile) break;  // a ring slot no step uses: no load
             const size_t off = (size_t)min(ra + s * kStride + r, rb - 1) * D;
 #pragma unroll
-            for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+            for (int t = 0; t < NF4; ++t) kf[s][t] = ld4_stream(kb + off + 4 * LPR * t);
 #pragma unroll
-            for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+            for (int t = 0; t < NF4; ++t) vf[s][t] = ld4_stream(vb + off + 4 * LPR * t);
         }
 
         // q of every head of the chunk, pre-scaled (zero for heads past nh;
@@ -352,9 +345,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
                     step(kf[s], vf[s], row);
                     const size_t off = (size_t)min(row + P * kStride, rb - 1) * D;
 #pragma unroll
-                    for (int t = 0; t < NF4; ++t) kf[s][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+                    for (int t = 0; t < NF4; ++t) kf[s][t] = ld4_stream(kb + off + 4 * LPR * t);
 #pragma unroll
-                    for (int t = 0; t < NF4; ++t) vf[s][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+                    for (int t = 0; t < NF4; ++t) vf[s][t] = ld4_stream(vb + off + 4 * LPR * t);
                 }
             }
             // tail: the remaining (fewer than 2P) steps, refilling only while a
@@ -368,10 +361,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
                         const size_t off = (size_t)min(row + P * kStride, rb - 1) * D;
 #pragma unroll
                         for (int t = 0; t < NF4; ++t)
-                            kf[s % P][t] = kv_load<NT>(kb + off + 4 * LPR * t);
+                            kf[s % P][t] = ld4_stream(kb + off + 4 * LPR * t);
 #pragma unroll
                         for (int t = 0; t < NF4; ++t)
-                            vf[s % P][t] = kv_load<NT>(vb + off + 4 * LPR * t);
+                            vf[s % P][t] = ld4_stream(vb + off + 4 * LPR * t);
                     }
                 }
             }
