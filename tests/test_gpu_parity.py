@@ -990,3 +990,52 @@ def test_prefill_wide_score_spread(dev):
     q, k, v = synth.prefill_inputs(w)
     o = _gpu_prefill(dev, w, q, k, v)
     _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), _vmax_prefill(w, v), "wide")
+
+
+# ------------------------------------------------- invariants on GPU outputs
+
+def test_prefill_future_rows_do_not_reach_earlier_rows(dev):
+    """Rewriting the K/V rows from row 192 on leaves the outputs of rows
+    0-191 bit for bit (the tiles those rows read end before row 192, and the
+    kernel is deterministic); the later rows change."""
+    w = synth.PrefillWorkload("fut", m=500, num_q_heads=12, heads_per_kv=6, head_dim=128,
+                              q_stride=12 * 128, kv_stride=2 * 128, seed=505)
+    q, k, v = synth.prefill_inputs(w)
+    o1 = _gpu_prefill(dev, w, q, k, v)
+    k2, v2 = k.copy(), v.copy()
+    rng = np.random.default_rng(506)
+    k2[192:] = rng.standard_normal(k2[192:].shape).astype(np.float32)
+    v2[192:] = rng.standard_normal(v2[192:].shape).astype(np.float32)
+    o2 = _gpu_prefill(dev, w, q, k2, v2)
+    assert np.array_equal(o1[:192], o2[:192])
+    assert not np.array_equal(o1[192:], o2[192:])
+
+
+def test_prefill_gqa_equals_mha_with_repeated_kv_heads(dev):
+    """GQA with 4 query heads per KV head gives the same bits as MHA over
+    K/V heads repeated consecutively (each query head's arithmetic is the
+    same; only the grouping of waves differs)."""
+    m, hq, hpk, d = 333, 8, 4, 64
+    hkv = hq // hpk
+    w = synth.PrefillWorkload("gqa", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d, kv_stride=hkv * d, seed=77)
+    q, k, v = synth.prefill_inputs(w)
+    o_gqa = _gpu_prefill(dev, w, q, k, v)
+    rep = lambda x: np.ascontiguousarray(
+        np.repeat(x.reshape(m, hkv, d), hpk, axis=1).reshape(m, hq * d))
+    w_mha = w.with_(heads_per_kv=1, kv_stride=hq * d)
+    o_mha = _gpu_prefill(dev, w_mha, q, rep(k), rep(v))
+    assert np.array_equal(o_gqa, o_mha)
+
+
+def test_decode_gqa_equals_mha_with_repeated_kv_heads(dev):
+    """The same for decode, within the bar (the work split differs with the
+    head count, so the summation order does too)."""
+    b, hq, hkv, d, t = 3, 12, 2, 128, 700
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, t, t, seed=88)
+    got = _gpu_decode(dev, w, q, k, v)
+    kr = np.ascontiguousarray(np.repeat(k, hq // hkv, axis=1))
+    vr = np.ascontiguousarray(np.repeat(v, hq // hkv, axis=1))
+    w_mha = w.with_(kv_heads=hq)
+    got_mha = _gpu_decode(dev, w_mha, q, kr, vr)
+    _assert_close(got, got_mha.astype(np.float64), _vmax_decode(w, v), "gqa vs mha")
