@@ -10,7 +10,9 @@
 // group walking every position of one head in sequence):
 //   unit  = (sequence b, KV head g, chunk of <= 8 Q heads of that group)
 //   split = a contiguous range of attended rows; one workgroup of NW waves
-//   wave  = a contiguous sub-range, streamed RPT = 64/LPR rows per step
+//           (with per-sequence lengths, each unit gets splits in proportion
+//           to its rows: prop_split)
+//   wave  = every NW-th step of the split's range, RPT = 64/LPR rows per step
 //   lane  = (row slot r, d-chunk c): LPR lanes cover one row's head_dim; lane
 //           c holds float4 chunks c, c+LPR, ... so each global_load_dwordx4
 //           of a row is LPR*16 contiguous bytes.
@@ -32,7 +34,8 @@
 // appends the current token (attn_decode_append), the split pass covers the
 // rows before it and the merge kernel folds the new row in as one more
 // partial state, scored from the new K row itself, and writes the new K and
-// V rows into the caches.
+// V rows into the caches (rotated first when the call applies rotary
+// embedding; the split pass then rotates q as it loads it).
 #pragma once
 
 #include "common.hpp"
@@ -47,7 +50,7 @@ struct DecodeArgs {
     const float *k;
     const float *v;
     float *out;
-    float *part;      // [units][n_split][HC][D + 2]: acc[D], m, l
+    float *part;      // [splits][HC][D + 2]: acc[D], m, l; splits numbered unit by unit
     // fused append (merge kernel only): new rows [B, Hkv, D], or null
     const float *k_new;
     const float *v_new;
