@@ -10,7 +10,7 @@
 namespace {
 
 bool head_dim_multiple_of_32(uint32_t d) { return d != 0 && d % 32 == 0; }
-bool head_dim_built(uint32_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+bool head_dim_built(uint32_t d) { return d >= 32 && d <= 256 && d % 32 == 0; }
 bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
 

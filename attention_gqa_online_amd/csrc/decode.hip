@@ -19,7 +19,26 @@ constexpr uint32_t kTargetWorkgroupsVarlen(uint32_t units) {
 }
 constexpr int kMinRowsPerWave = 32;
 
-constexpr int lanes_per_row(int d) { return d == 32 ? 8 : 16; }
+// Lanes that hold one K/V row: 16, or 8 where a lane's share of the row
+// would not be whole float4 chunks (head_dim / 4 not a multiple of 16).
+constexpr int lanes_per_row(int d) { return (d / 4) % 16 == 0 ? 16 : 8; }
+
+// Largest head chunk (at most 8) whose row-slot accumulators, [slots][HC][d]
+// floats, fit the 160 KiB of LDS next to the kernel's other arrays, and whose
+// registers (q and acc: about 10 per float4 of a lane's row share and head,
+// the ring 16 per float4, about 100 more) fit the 512 a lane has at one wave
+// per SIMD without spilling to scratch memory.
+constexpr int max_head_chunk(int d) {
+    const int slots = kDecodeWaves * (64 / lanes_per_row(d));
+    const int lds_hc = (160 * 1024 - 4096) / (slots * d * 4);
+    const int nf4 = d / lanes_per_row(d) / 4;  // float4 of a lane's row share
+    const int reg_hc = (500 - 100 - 16 * nf4) / (10 * nf4);
+    const int hc = lds_hc < reg_hc ? lds_hc : reg_hc;
+    return hc < 8 ? hc : 8;
+}
+
+// Threads of a merge workgroup: one per d, rounded up to whole waves.
+constexpr int merge_threads(int d) { return d <= 64 ? d : (d + 63) / 64 * 64; }
 
 // Pass 1 writes one partial state per (unit, split, head); pass 2, ordered
 // after it on the same stream, merges the splits of every (unit, head). With
@@ -49,22 +68,32 @@ hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStrea
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_merge_kernel<D, HC>), dim3(units * HC), dim3(D), 0, stream, args);
+    hipLaunchKernelGGL((decode_merge_kernel<D, HC>), dim3(units * HC), dim3(merge_threads(D)), 0,
+                       stream, args);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(uint32_t hc, const DecodeArgs &args, uint32_t units, uint32_t n_split,
                     hipStream_t stream) {
+    // head chunks beyond max_head_chunk(D) are never planned (nor built)
     switch (hc) {
     case 1: return launch_hc<D, 1>(args, units, n_split, stream);
     case 2: return launch_hc<D, 2>(args, units, n_split, stream);
     case 3: return launch_hc<D, 3>(args, units, n_split, stream);
     case 4: return launch_hc<D, 4>(args, units, n_split, stream);
-    case 5: return launch_hc<D, 5>(args, units, n_split, stream);
-    case 6: return launch_hc<D, 6>(args, units, n_split, stream);
-    case 7: return launch_hc<D, 7>(args, units, n_split, stream);
-    case 8: return launch_hc<D, 8>(args, units, n_split, stream);
+    case 5:
+        if constexpr (max_head_chunk(D) >= 5) return launch_hc<D, 5>(args, units, n_split, stream);
+        return hipErrorInvalidValue;
+    case 6:
+        if constexpr (max_head_chunk(D) >= 6) return launch_hc<D, 6>(args, units, n_split, stream);
+        return hipErrorInvalidValue;
+    case 7:
+        if constexpr (max_head_chunk(D) >= 7) return launch_hc<D, 7>(args, units, n_split, stream);
+        return hipErrorInvalidValue;
+    case 8:
+        if constexpr (max_head_chunk(D) >= 8) return launch_hc<D, 8>(args, units, n_split, stream);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -79,7 +108,19 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     DecodePlan p{};
     if (kv_heads == 0 || num_heads < kv_heads) return p;  // no head: no work, no workspace
     const uint32_t hpk = num_heads / kv_heads;
-    p.n_chunks = ceil_div(hpk, 8);
+    uint32_t max_hc = 8;
+    switch (head_dim) {  // the built head sizes (see max_head_chunk)
+    case 32: max_hc = max_head_chunk(32); break;
+    case 64: max_hc = max_head_chunk(64); break;
+    case 96: max_hc = max_head_chunk(96); break;
+    case 128: max_hc = max_head_chunk(128); break;
+    case 160: max_hc = max_head_chunk(160); break;
+    case 192: max_hc = max_head_chunk(192); break;
+    case 224: max_hc = max_head_chunk(224); break;
+    case 256: max_hc = max_head_chunk(256); break;
+    default: break;
+    }
+    p.n_chunks = ceil_div(hpk, max_hc);
     p.head_chunk = ceil_div(hpk, p.n_chunks);
     p.units = batch * kv_heads * p.n_chunks;
     p.w0 = (window > 0 && total_seq > window) ? total_seq - window : 0;
@@ -154,7 +195,11 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
     switch (head_dim) {
     case 32: return launch_d<32>(hc, a, u, ns, stream);
     case 64: return launch_d<64>(hc, a, u, ns, stream);
+    case 96: return launch_d<96>(hc, a, u, ns, stream);
     case 128: return launch_d<128>(hc, a, u, ns, stream);
+    case 160: return launch_d<160>(hc, a, u, ns, stream);
+    case 192: return launch_d<192>(hc, a, u, ns, stream);
+    case 224: return launch_d<224>(hc, a, u, ns, stream);
     case 256: return launch_d<256>(hc, a, u, ns, stream);
     default: return hipErrorInvalidValue;
     }

@@ -459,21 +459,21 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
 }
 
-// Sum over the D threads of a workgroup (D in {32, 64, 128, 256}).
-template <int D>
+// Sum over the NT threads of a workgroup (NT = 32, or a multiple of 64).
+template <int NT>
 __device__ __forceinline__ float block_sum(float x) {
-    constexpr int W = D < 64 ? D : 64;
+    constexpr int W = NT < 64 ? NT : 64;
 #pragma unroll
     for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, W);
-    if constexpr (D <= 64) {
+    if constexpr (NT <= 64) {
         return x;
     } else {
-        __shared__ float red[D / 64];
+        __shared__ float red[NT / 64];
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
         __syncthreads();
         float t = 0.f;
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) t += red[i];
+        for (int i = 0; i < NT / 64; ++i) t += red[i];
         return t;
     }
 }
@@ -486,8 +486,13 @@ __device__ __forceinline__ float block_sum(float x) {
 constexpr int kMaxSplit = 1024;
 
 template <int D, int HC>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge_kernel(
+    DecodeArgs a) {
+    // one thread per d, rounded up to whole waves; threads past D re-read
+    // element D - 1, store nothing and add 0 to the new row's score
+    constexpr int NT = D <= 64 ? D : (D + 63) / 64 * 64;
+    const bool live = (int)threadIdx.x < D;
+    const int tid = live ? (int)threadIdx.x : D - 1;
     const uint32_t unit = blockIdx.x / HC;
     const int hh = blockIdx.x % HC;
     const uint32_t chunk = unit % a.n_chunks;
@@ -502,12 +507,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     size_t first = (size_t)unit * a.n_split;  // the unit's first split index
     if (a.lens != nullptr) {
         if (!sr.valid) {  // invalid length: NaN output, nothing appended
-            a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
+            if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
             return;
         }
         if (ns != 0) {  // the split pass ran with the proportional table
-            constexpr int W = D < 64 ? D : 64;
-            const int lane = tid & 63;
+            constexpr int W = NT < 64 ? NT : 64;
+            const int lane = threadIdx.x & 63;
             const PropHit ph = prop_find<W>(a, prop_total<W>(a, lane), unit, true, lane);
             first = ph.first;
             ns = ph.n;
@@ -560,10 +565,10 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
             qd = rope_half1(qd, qp[partner], cc, ss, lo);
         }
         qd *= a.qscale;
-        M = block_sum<D>(qd * kn);  // the new row's score, log2 units
+        M = block_sum<NT>(live ? qd * kn : 0.f);  // the new row's score, log2 units
         num = vn;
         den = 1.f;
-        if (hl0 + hh == 0) {  // one writer per (sequence, KV head)
+        if (hl0 + hh == 0 && live) {  // one writer per (sequence, KV head)
             const size_t dst = ((size_t)bg * a.max_seq + sr.pos) * D + tid;
             a.k_dst[dst] = kn;
             a.v_dst[dst] = vn;
@@ -575,7 +580,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
         fold_round();
     }
     // den is 0 only for an idle sequence (no rows, nothing appended)
-    a.out[((size_t)b * a.num_heads + h) * D + tid] = den > 0.f ? num / den : 0.f;
+    if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = den > 0.f ? num / den : 0.f;
 }
 
 }  // namespace attn

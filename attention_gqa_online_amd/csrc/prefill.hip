@@ -70,9 +70,13 @@ __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
 // 16-byte chunk index of a K/V element row inside an LDS tile row, XOR-
 // swizzled by the row so that the 32 lanes of an MFMA operand read (one row
 // each, same logical chunk) land in different LDS banks without padding.
+// Width of the XOR swizzle: the largest of 16, 8, 4 that divides the row's
+// chunk count, so a swizzled chunk stays inside its row.
+constexpr int swz_width(int d) { return (d / 4) % 16 == 0 ? 16 : (d / 4) % 8 == 0 ? 8 : 4; }
+
 template <int D>
 __device__ __forceinline__ int swz_chunk(int row, int chunk) {
-    constexpr int SW = D / 4 < 16 ? D / 4 : 16;
+    constexpr int SW = swz_width(D);
     return chunk ^ (row & (SW - 1));
 }
 
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
             for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
             // chunk 2u + half of row j sits at (2u + half) ^ (j mod SW) =
             // 2u ^ xh: one XOR with a constant per step, no per-step register
-            constexpr int SW = D / 4 < 16 ? D / 4 : 16;
+            constexpr int SW = swz_width(D);
             int xh = (j & (SW - 1)) ^ half;
             asm volatile("" : "+v"(xh));
             const float *krow = sk + j * D;
@@ -399,7 +403,11 @@ hipError_t launch_prefill(const float *q, const float *k, const float *v, float 
     switch (head_dim) {
     case 32: return launch_d<32>(a, grid, stream);
     case 64: return launch_d<64>(a, grid, stream);
+    case 96: return launch_d<96>(a, grid, stream);
     case 128: return launch_d<128>(a, grid, stream);
+    case 160: return launch_d<160>(a, grid, stream);
+    case 192: return launch_d<192>(a, grid, stream);
+    case 224: return launch_d<224>(a, grid, stream);
     case 256: return launch_d<256>(a, grid, stream);
     default: return hipErrorInvalidValue;
     }

@@ -35,8 +35,8 @@
  *   - Pointers must be 16-byte aligned; strides are in elements and must be
  *     multiples of 4 (every row starts 16-byte aligned).
  *   - head_dim must be a multiple of 32 (ATTN_ERR_INVALID otherwise); this
- *     build supports head_dim in {32, 64, 128, 256} (ATTN_ERR_UNSUPPORTED for
- *     the other multiples of 32).
+ *     build supports every multiple of 32 from 32 to 256 (ATTN_ERR_UNSUPPORTED
+ *     above 256).
  *
  * The softmax is evaluated in one pass with a running maximum, a correction
  * factor and a running sum (online softmax), so no score matrix is stored;

@@ -77,7 +77,7 @@ def test_prefill_page_constructor_cases(lib, golden):
 
 def test_prefill_argument_rules(lib):
     assert _prefill(lib, d=0) == INVALID
-    assert _prefill(lib, d=96) == UNSUPPORTED            # multiple of 32, not built
+    assert _prefill(lib, d=288) == UNSUPPORTED           # multiple of 32 past 256
     assert _prefill(lib, d=320) == UNSUPPORTED
     assert _prefill(lib, hq=5, hpk=2) == INVALID         # Hq not a multiple of hpk
     assert _prefill(lib, q_stride=4 * 32 - 4) == INVALID # row too short for Q heads
@@ -101,7 +101,7 @@ def _decode(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, t=64, window=0,
 
 def test_decode_argument_rules(lib):
     assert _decode(lib, d=48) == INVALID
-    assert _decode(lib, d=224) == UNSUPPORTED
+    assert _decode(lib, d=288) == UNSUPPORTED
     assert _decode(lib, hkv=0) == INVALID
     assert _decode(lib, hq=12, hkv=5) == INVALID
     assert _decode(lib, t=0) == INVALID                     # nothing to attend
@@ -162,7 +162,7 @@ def _decode_append(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, pos=63, window=0,
 
 def test_decode_append_argument_rules(lib):
     assert _decode_append(lib, d=48) == INVALID
-    assert _decode_append(lib, d=160) == UNSUPPORTED
+    assert _decode_append(lib, d=352) == UNSUPPORTED
     assert _decode_append(lib, hkv=0) == INVALID
     assert _decode_append(lib, hq=12, hkv=5) == INVALID
     assert _decode_append(lib, pos=64, max_seq=64) == INVALID   # past the cache
@@ -183,7 +183,7 @@ def _decode_rope(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, pos=63, window=0,
 
 def test_decode_rope_append_argument_rules(lib):
     assert _decode_rope(lib, d=48) == INVALID
-    assert _decode_rope(lib, d=192) == UNSUPPORTED
+    assert _decode_rope(lib, d=384) == UNSUPPORTED
     assert _decode_rope(lib, hkv=0) == INVALID
     assert _decode_rope(lib, hq=12, hkv=5) == INVALID
     assert _decode_rope(lib, pos=64, max_seq=64) == INVALID
@@ -221,7 +221,7 @@ def _varlen(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, bound=64, window=0,
 
 def test_decode_varlen_argument_rules(lib):
     assert _varlen(lib, d=48) == INVALID
-    assert _varlen(lib, d=96) == UNSUPPORTED
+    assert _varlen(lib, d=416) == UNSUPPORTED
     assert _varlen(lib, hkv=0) == INVALID
     assert _varlen(lib, hq=12, hkv=5) == INVALID
     assert _varlen(lib, bound=0) == INVALID
@@ -246,7 +246,7 @@ def _append_varlen(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, bound=64, window=0
 
 def test_decode_append_varlen_argument_rules(lib):
     assert _append_varlen(lib, d=48) == INVALID
-    assert _append_varlen(lib, d=160) == UNSUPPORTED
+    assert _append_varlen(lib, d=448) == UNSUPPORTED
     assert _append_varlen(lib, hkv=0) == INVALID
     assert _append_varlen(lib, bound=0) == INVALID
     assert _append_varlen(lib, bound=65, max_seq=64) == INVALID

@@ -117,6 +117,13 @@ DECODE_SWEEP = [
     (64, 8, 4, 128, 300, 300, 0),     # 256 units: one split, output written directly
     (80, 12, 4, 64, 200, 170, 50),    # 320 units, one split, windowed
     (1, 32, 8, 128, 9000, 9000, 4096),
+    # head sizes held in 8 lanes per row, and capped head chunks
+    (2, 12, 2, 96, 300, 257, 0),
+    (1, 8, 1, 160, 500, 480, 100),    # 8 heads per KV head -> chunks of 4 (cap 6)
+    (3, 4, 4, 160, 200, 130, 7),
+    (2, 6, 2, 192, 300, 299, 0),
+    (1, 10, 2, 224, 600, 513, 0),     # 5 per KV head -> chunks of 3 and 2 (cap 4)
+    (64, 4, 4, 224, 100, 77, 0),      # 256 units, one split
 ]
 
 
@@ -198,6 +205,8 @@ DECODE_APPEND_CASES = [
     (64, 8, 4, 128, 300, 299, 0),      # 256 units
     (2, 8, 1, 256, 600, 512, 100),
     (1, 32, 8, 128, 9000, 8999, 4096),
+    (2, 8, 2, 96, 300, 250, 0),
+    (1, 12, 2, 224, 400, 399, 31),
 ]
 
 
@@ -411,6 +420,8 @@ ROWS_CASES = [
     (300, 3, 128, 8, 512, 211),
     (129, 1, 256, 4, 130, 1),
     (2048, 4, 128, 0, 4096, 0),          # the Qwen-shaped prefill's K/V
+    (33, 2, 96, 4, 40, 3),
+    (70, 3, 224, 8, 80, 9),
 ]
 
 
@@ -495,6 +506,7 @@ VARLEN_CASES = [
     (64, 8, 4, 128, 200, 200, 0, 3),     # many units: single-split plan (direct)
     (2, 9, 1, 128, 3000, 3000, 0, 0),    # two head chunks
     (32, 12, 2, 128, 4096, 4096, 0, 2),  # the decode workload's shape, mixed lengths
+    (4, 8, 2, 160, 300, 300, 0, 1),
 ]
 
 
@@ -706,6 +718,7 @@ PREFILL_SWEEP = [
     (129, 12, 3, 64), (300, 5, 5, 128), (257, 6, 2, 128), (1000, 8, 4, 128),
     (200, 3, 1, 256), (100, 16, 8, 256), (450, 10, 5, 32), (97, 9, 9, 64),
     (1000, 28, 7, 128),
+    (200, 6, 3, 96), (64, 2, 1, 96), (129, 4, 2, 160), (300, 8, 4, 192), (97, 6, 6, 224),
 ]
 
 
