@@ -33,6 +33,11 @@ import still succeeds, but the first call raises.
                               positions, batch, num_heads, kv_heads, head_dim,
                               max_seq, seq_bound, window, scale, workspace,
                               workspace_bytes=None, stream=None)
+    attn_decode_rope_append_varlen(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache,
+                                   v_cache, out, positions, batch, num_heads,
+                                   kv_heads, head_dim, max_seq, seq_bound,
+                                   window, scale, workspace,
+                                   workspace_bytes=None, stream=None)
     attn_status_string(status) -> str
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed, and
@@ -49,8 +54,8 @@ __all__ = [
     "ATTN_ERR_HIP", "SO_PATH", "library", "attn_prefill_causal",
     "attn_decode_workspace_bytes", "attn_decode", "kv_append",
     "attn_decode_append", "attn_decode_rope_append", "kv_append_rows",
-    "attn_decode_varlen", "attn_decode_append_varlen", "attn_status_string",
-    "decode_workspace",
+    "attn_decode_varlen", "attn_decode_append_varlen", "attn_decode_rope_append_varlen",
+    "attn_status_string", "decode_workspace",
 ]
 
 SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -60,7 +65,7 @@ ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 EXPORTS = ("attn_prefill_causal", "attn_decode_workspace_bytes", "attn_decode",
            "kv_append", "attn_decode_append", "attn_decode_rope_append",
            "kv_append_rows", "attn_decode_varlen", "attn_decode_append_varlen",
-           "attn_status_string")
+           "attn_decode_rope_append_varlen", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -109,6 +114,9 @@ def library() -> ctypes.CDLL:
             ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         lib.attn_decode_append_varlen.restype = ctypes.c_int
         lib.attn_decode_append_varlen.argtypes = [_vp] * 7 + [_u32] * 7 + [
+            ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        lib.attn_decode_rope_append_varlen.restype = ctypes.c_int
+        lib.attn_decode_rope_append_varlen.argtypes = [_vp] * 9 + [_u32] * 7 + [
             ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -309,3 +317,24 @@ def attn_decode_append_varlen(q, k_new, v_new, k_cache, v_cache, out, positions,
         seq_bound, window, float(scale), _ptr(workspace, "workspace"), int(workspace_bytes),
         _stream(stream))
     _check("attn_decode_append_varlen", st)
+
+
+def attn_decode_rope_append_varlen(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache, out,
+                                   positions, batch, num_heads, kv_heads, head_dim, max_seq,
+                                   seq_bound, window, scale, workspace, workspace_bytes=None,
+                                   stream=None) -> None:
+    """Rotary decode step with per-sequence positions (int32 device tensor,
+    read as uint32) and per-sequence tables ``cos_t``/``sin_t``
+    (``[batch, head_dim/2]``, row b for positions[b])."""
+    n_src = batch * kv_heads * head_dim
+    n_cache = batch * kv_heads * max_seq * head_dim
+    n_tab = batch * (head_dim // 2)
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    st = library().attn_decode_rope_append_varlen(
+        _ptr(q_raw, "q_raw", batch * num_heads * head_dim), _ptr(k_raw, "k_raw", n_src),
+        _ptr(v_raw, "v_raw", n_src), _ptr(cos_t, "cos_t", n_tab), _ptr(sin_t, "sin_t", n_tab),
+        _ptr(k_cache, "k_cache", n_cache), _ptr(v_cache, "v_cache", n_cache),
+        _ptr(out, "out", batch * num_heads * head_dim), _ptr(positions, "positions", batch),
+        batch, num_heads, kv_heads, head_dim, max_seq, seq_bound, window, float(scale),
+        _ptr(workspace, "workspace"), int(workspace_bytes), _stream(stream))
+    _check("attn_decode_rope_append_varlen", st)

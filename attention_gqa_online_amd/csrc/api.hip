@@ -91,6 +91,8 @@ attn_status attn_decode(const float *q, const float *k_cache, const float *v_cac
                                         nullptr, stream));
 }
 
+}  // extern "C"
+
 namespace {
 
 attn_status decode_step(const float *q, const float *k_new, const float *v_new,
@@ -101,6 +103,8 @@ attn_status decode_step(const float *q, const float *k_new, const float *v_new,
                         size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace
+
+extern "C" {
 
 attn_status attn_decode_append(const float *q, const float *k_new, const float *v_new,
                                float *k_cache, float *v_cache, float *out, uint32_t batch,
@@ -224,13 +228,17 @@ attn_status attn_decode_varlen(const float *q, const float *k_cache, const float
                                         nullptr, stream, &vl));
 }
 
-attn_status attn_decode_append_varlen(const float *q, const float *k_new, const float *v_new,
-                                      float *k_cache, float *v_cache, float *out,
-                                      const uint32_t *positions, uint32_t batch,
-                                      uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
-                                      uint32_t max_seq, uint32_t seq_bound, uint32_t window,
-                                      float scale, void *workspace, size_t workspace_bytes,
-                                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+attn_status decode_step_varlen(const float *q, const float *k_new, const float *v_new,
+                               const float *cos_t, const float *sin_t, float *k_cache,
+                               float *v_cache, float *out, const uint32_t *positions,
+                               uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
+                               uint32_t head_dim, uint32_t max_seq, uint32_t seq_bound,
+                               uint32_t window, float scale, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
     if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
     if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
     if (seq_bound == 0 || seq_bound > max_seq) return ATTN_ERR_INVALID;
@@ -243,10 +251,11 @@ attn_status attn_decode_append_varlen(const float *q, const float *k_new, const 
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned4(positions))
         return ATTN_ERR_INVALID;
+    const uint32_t cs_stride = cos_t != nullptr ? head_dim / 2 : 0;  // one table per sequence
     if (num_heads == 0) {  // nothing to attend: the appends alone
         return from_hip(attn::launch_kv_append(k_new, v_new, k_cache, v_cache, batch, kv_heads,
-                                               head_dim, max_seq, seq_bound, stream, nullptr,
-                                               nullptr, positions));
+                                               head_dim, max_seq, seq_bound, stream, cos_t,
+                                               sin_t, positions, cs_stride));
     }
     if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
     const attn::DecodePlan plan =
@@ -254,11 +263,43 @@ attn_status attn_decode_append_varlen(const float *q, const float *k_new, const 
     if (plan.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes))
         return ATTN_ERR_INVALID;
     if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
-    const attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, nullptr, nullptr};
+    const attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, cos_t, sin_t, cs_stride};
     const attn::DecodeVarlen vl{positions, 1, seq_bound, window};
     return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
                                         head_dim, max_seq, seq_bound, scale, workspace, &app,
                                         stream, &vl));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_append_varlen(const float *q, const float *k_new, const float *v_new,
+                                      float *k_cache, float *v_cache, float *out,
+                                      const uint32_t *positions, uint32_t batch,
+                                      uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                                      uint32_t max_seq, uint32_t seq_bound, uint32_t window,
+                                      float scale, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    return decode_step_varlen(q, k_new, v_new, nullptr, nullptr, k_cache, v_cache, out,
+                              positions, batch, num_heads, kv_heads, head_dim, max_seq,
+                              seq_bound, window, scale, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_rope_append_varlen(const float *q_raw, const float *k_raw,
+                                           const float *v_raw, const float *cos_t,
+                                           const float *sin_t, float *k_cache,
+                                           float *v_cache, float *out,
+                                           const uint32_t *positions, uint32_t batch,
+                                           uint32_t num_heads, uint32_t kv_heads,
+                                           uint32_t head_dim, uint32_t max_seq,
+                                           uint32_t seq_bound, uint32_t window, float scale,
+                                           void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+    if (batch != 0 && (!aligned16(cos_t) || !aligned16(sin_t))) return ATTN_ERR_INVALID;
+    return decode_step_varlen(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache, out,
+                              positions, batch, num_heads, kv_heads, head_dim, max_seq,
+                              seq_bound, window, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

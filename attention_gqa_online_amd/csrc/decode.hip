@@ -184,6 +184,7 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
         a.position = total_seq - 1;
         a.cos_t = append->cos_t;
         a.sin_t = append->sin_t;
+        a.cs_stride = append->cs_stride;
     }
     if (varlen) {  // total_seq is then the bound the plan was made for
         a.lens = varlen->lens;

@@ -58,9 +58,11 @@ struct DecodeArgs {
     float *v_dst;
     uint32_t position;
     // rotary embedding of the current token (rotate-half), or null:
-    // cos/sin [D/2] for `position`, applied to q and to the new K rows
+    // cos/sin [D/2] for `position`, applied to q and to the new K rows;
+    // sequence b's table starts cs_stride * b floats in (0: one shared table)
     const float *cos_t;
     const float *sin_t;
+    uint32_t cs_stride;
     // per-sequence lengths, or null (then every sequence has the rows
     // [w0, total_seq) before the appended one): sequence b then has
     // T_b = lens[b] + len_add rows, valid when T_b <= seq_bound; with an
@@ -283,8 +285,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
                     const int d0 = 4 * (c + LPR * t);
                     const bool lo = d0 < D / 2;
                     const float4 xp = ld4(qh + 4 * LPR * t + (lo ? D / 2 : -D / 2));
-                    const float4 cc = ld4(a.cos_t + (d0 % (D / 2)));
-                    const float4 ss = ld4(a.sin_t + (d0 % (D / 2)));
+                    const size_t ci = (size_t)b * a.cs_stride + (d0 % (D / 2));
+                    const float4 cc = ld4(a.cos_t + ci);
+                    const float4 ss = ld4(a.sin_t + ci);
                     qv[hh][t] = rope_half(qv[hh][t], xp, cc, ss, lo);
                 }
             }
@@ -560,7 +563,8 @@ __global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge
         if (a.cos_t != nullptr) {  // rotate the new K row and q (rotate-half)
             const bool lo = tid < D / 2;
             const int partner = lo ? tid + D / 2 : tid - D / 2;
-            const float cc = a.cos_t[tid % (D / 2)], ss = a.sin_t[tid % (D / 2)];
+            const size_t ci = (size_t)b * a.cs_stride + tid % (D / 2);
+            const float cc = a.cos_t[ci], ss = a.sin_t[ci];
             kn = rope_half1(kn, knp[partner], cc, ss, lo);
             qd = rope_half1(qd, qp[partner], cc, ss, lo);
         }

@@ -47,6 +47,7 @@ struct DecodeAppend {
     float *v_cache;
     const float *cos_t = nullptr;
     const float *sin_t = nullptr;
+    uint32_t cs_stride = 0;  // floats between sequences' tables (0: one shared table)
 };
 
 hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_cache,
@@ -71,7 +72,7 @@ hipError_t launch_kv_append(const float *k_src, const float *v_src, float *k_cac
                             uint32_t head_dim, uint32_t max_seq, uint32_t position,
                             hipStream_t stream, const float *cos_t = nullptr,
                             const float *sin_t = nullptr,
-                            const uint32_t *positions = nullptr);
+                            const uint32_t *positions = nullptr, uint32_t cs_stride = 0);
 
 // Rows [0, m) of packed K/V ([m, kv_stride]) into [kv_heads, max_seq, d]
 // caches from row `position` on.

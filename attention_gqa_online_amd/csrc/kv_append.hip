@@ -15,8 +15,8 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(
     const float *__restrict__ k_src, const float *__restrict__ v_src, float *__restrict__ k_cache,
     float *__restrict__ v_cache, const float *__restrict__ cos_t, const float *__restrict__ sin_t,
-    const uint32_t *__restrict__ positions, uint32_t kv_heads, uint32_t n4, uint32_t d4,
-    uint32_t max_seq, uint32_t position) {
+    const uint32_t *__restrict__ positions, uint32_t cs_stride, uint32_t kv_heads, uint32_t n4,
+    uint32_t d4, uint32_t max_seq, uint32_t position) {
     const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
     if (idx >= n4) return;
     const uint32_t bg = idx / d4;  // b * kv_heads + g
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
         const uint32_t h4 = d4 / 2;  // half a row, in float4 units
         const bool lo = c < h4;
         const float4 xp = ld4(k_src + 4 * (size_t)(lo ? idx + h4 : idx - h4));
-        const uint32_t i = 4 * (lo ? c : c - h4);
+        const size_t i = (size_t)(bg / kv_heads) * cs_stride + 4 * (lo ? c : c - h4);
         kx = rope_half(kx, xp, ld4(cos_t + i), ld4(sin_t + i), lo);
     }
     st4(k_cache + dst, kx);
@@ -45,13 +45,13 @@ hipError_t launch_kv_append(const float *k_src, const float *v_src, float *k_cac
                             float *v_cache, uint32_t batch, uint32_t kv_heads,
                             uint32_t head_dim, uint32_t max_seq, uint32_t position,
                             hipStream_t stream, const float *cos_t, const float *sin_t,
-                            const uint32_t *positions) {
+                            const uint32_t *positions, uint32_t cs_stride) {
     const uint32_t d4 = head_dim / 4;
     const uint32_t n4 = batch * kv_heads * d4;  // bounded by the caller
     const uint32_t grid = (n4 + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(kThreads), 0, stream, k_src, v_src,
-                       k_cache, v_cache, cos_t, sin_t, positions, kv_heads, n4, d4, max_seq,
-                       position);
+                       k_cache, v_cache, cos_t, sin_t, positions, cs_stride, kv_heads, n4, d4,
+                       max_seq, position);
     return hipGetLastError();
 }
 

@@ -19,6 +19,9 @@
  *   attn_decode_varlen    attn_decode with one length per sequence
  *   attn_decode_append_varlen
  *                         attn_decode_append with one position per sequence
+ *   attn_decode_rope_append_varlen
+ *                         attn_decode_rope_append with one position (and one
+ *                         rotary table) per sequence
  *
  * Common rules
  *   - Every tensor is fp32, row-major. Every pointer is a DEVICE pointer owned
@@ -317,6 +320,32 @@ attn_status attn_decode_append_varlen(const float *q, const float *k_new,
                                       uint32_t seq_bound, uint32_t window,
                                       float scale, void *workspace,
                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The rotary decode step of a batch whose sequences sit at their own
+ * positions: attn_decode_rope_append per sequence, with sequence b's table
+ * for its own position positions[b] (the fused kernel of glia honeycrisp
+ * "attention.rs" page, which serves one sequence, taken over a batch as in
+ * attn_decode_append_varlen).
+ *
+ *   cos_t, sin_t  [batch, head_dim / 2]  row b: cos and sin of pair i's angle
+ *                                        at positions[b]
+ *   other arguments as attn_decode_append_varlen (q_raw, k_raw, v_raw as in
+ *   attn_decode_rope_append).
+ *
+ * Errors and zero-work cases: as attn_decode_append_varlen, plus null or
+ * misaligned (16-byte) cos_t / sin_t.
+ */
+attn_status attn_decode_rope_append_varlen(const float *q_raw, const float *k_raw,
+                                           const float *v_raw, const float *cos_t,
+                                           const float *sin_t, float *k_cache,
+                                           float *v_cache, float *out,
+                                           const uint32_t *positions, uint32_t batch,
+                                           uint32_t num_heads, uint32_t kv_heads,
+                                           uint32_t head_dim, uint32_t max_seq,
+                                           uint32_t seq_bound, uint32_t window,
+                                           float scale, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char *attn_status_string(attn_status s);

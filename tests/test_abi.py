@@ -260,3 +260,37 @@ def test_decode_append_varlen_argument_rules(lib):
     assert _append_varlen(lib, ws_bytes=0) == INVALID
     assert _append_varlen(lib, b=0) == OK
     assert _append_varlen(lib, b=0, ptrs=(0,) * 7) == OK
+
+
+def _rope_varlen(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, bound=64, window=0,
+                 scale=0.088, ws=P, ws_bytes=1 << 30, ptrs=(P,) * 9):
+    return lib.attn_decode_rope_append_varlen(*ptrs, b, hq, hkv, d, max_seq, bound, window,
+                                              ctypes.c_float(scale), ws, ws_bytes, None)
+
+
+def test_decode_rope_append_varlen_argument_rules(lib):
+    assert _rope_varlen(lib, d=48) == INVALID
+    assert _rope_varlen(lib, d=480) == UNSUPPORTED
+    assert _rope_varlen(lib, hkv=0) == INVALID
+    assert _rope_varlen(lib, bound=65, max_seq=64) == INVALID
+    assert _rope_varlen(lib, scale=float("nan")) == INVALID
+    for i in range(8):   # q, k, v, cos, sin, caches, out: null, then misaligned
+        for bad in (0, P + 4):
+            ptrs = tuple(bad if j == i else P for j in range(9))
+            assert _rope_varlen(lib, ptrs=ptrs) == INVALID, (i, bad)
+    assert _rope_varlen(lib, ptrs=(P,) * 8 + (0,)) == INVALID      # positions
+    assert _rope_varlen(lib, ws_bytes=0) == INVALID
+    assert _rope_varlen(lib, b=0, ptrs=(0,) * 9) == OK
+
+
+def test_library_exports_no_other_c_symbols(lib):
+    """The shared library's unmangled exports are exactly the header's."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", A.SO_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    c_names = {n for n in names if not n.startswith("_Z")}
+    assert c_names == set(_declared_functions())

@@ -1052,3 +1052,69 @@ def test_decode_gqa_equals_mha_with_repeated_kv_heads(dev):
     w_mha = w.with_(kv_heads=hq)
     got_mha = _gpu_decode(dev, w_mha, q, kr, vr)
     _assert_close(got, got_mha.astype(np.float64), _vmax_decode(w, v), "gqa vs mha")
+
+
+@pytest.mark.parametrize("case", [(5, 12, 2, 128, 300, 300, 0), (4, 8, 8, 64, 90, 90, 17),
+                                  (3, 10, 2, 224, 200, 150, 0), (32, 12, 2, 128, 4096, 4096, 0)],
+                         ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_bd{}_w{}".format(*c))
+def test_decode_rope_append_varlen_matches_oracle(dev, case):
+    """Rotary decode step with one position and one angle table per sequence
+    against the oracle's fused step run sequence by sequence."""
+    b, hq, hkv, d, ms, bound, win = case
+    seed = sum(case) % 863
+    w = synth.DecodeWorkload("rv", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, window=win, seed=seed)
+    q, k, v = synth.decode_inputs(w)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=seed + 1)
+    pos = synth.seq_lengths(b, bound, seed=seed + 2) - 1
+    tabs = [synth.rope_tables(d, int(p)) for p in pos]
+    cos_t = np.ascontiguousarray(np.stack([t[0] for t in tabs]))
+    sin_t = np.ascontiguousarray(np.stack([t[1] for t in tabs]))
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    out = torch.full((b, hq, d), float("nan"), device=dev)
+    ws = torch.full((A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win),), 0xFF,
+                    dtype=torch.uint8, device=dev)
+    A.attn_decode_rope_append_varlen(
+        torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev),
+        torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev), kd, vd, out,
+        torch.from_numpy(pos.astype(np.int32)).to(dev), b, hq, hkv, d, ms, bound, win,
+        w.scale, ws)
+    torch.cuda.synchronize()
+    k0 = k.copy()
+    ref = np.empty((b, hq, d))
+    for i in range(b):   # the oracle's fused step, sequence by sequence (updates k, v)
+        ref[i] = oracle.decode_rope_append(q[i:i + 1], kn[i:i + 1], vn[i:i + 1], cos_t[i],
+                                           sin_t[i], k[i:i + 1], v[i:i + 1], 1, hq, hkv, d, ms,
+                                           int(pos[i]), win, w.scale)[0]
+    kc, vc = kd.cpu().numpy(), vd.cpu().numpy()
+    assert np.array_equal(vc, v)
+    for i in range(b):
+        keep = np.arange(ms) != pos[i]
+        assert np.array_equal(kc[i][:, keep], k0[i][:, keep])
+        err = np.abs(kc[i, :, pos[i]].astype(np.float64) - k[i, :, pos[i]])
+        assert np.all(err <= _rope_row_bound(kn[i])), (i, float(err.max()))
+    _assert_close(out.cpu().numpy(), ref, _vmax_varlen(w, v, pos, plus=1), str(case))
+
+
+def test_decode_rope_append_varlen_no_heads_rotates_each_row(dev):
+    """num_heads == 0: each sequence appends its row rotated by its own table."""
+    b, hkv, d, ms, bound = 3, 2, 64, 16, 12
+    ks, vs = synth.append_inputs(b, hkv, d, seed=9)
+    pos = np.array([11, 0, 5], np.uint32)
+    tabs = [synth.rope_tables(d, 100.0 * (i + 1)) for i in range(b)]
+    cos_t = np.ascontiguousarray(np.stack([t[0] for t in tabs]))
+    sin_t = np.ascontiguousarray(np.stack([t[1] for t in tabs]))
+    kc = torch.full((b, hkv, ms, d), -2.0, device=dev)
+    vc = torch.full((b, hkv, ms, d), 3.0, device=dev)
+    A.attn_decode_rope_append_varlen(
+        0, torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev),
+        torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev), kc, vc, 0,
+        torch.from_numpy(pos.astype(np.int32)).to(dev), b, 0, hkv, d, ms, bound, 0, 0.125, None)
+    torch.cuda.synchronize()
+    kn, vn = kc.cpu().numpy(), vc.cpu().numpy()
+    for i in range(b):
+        assert np.array_equal(vn[i, :, pos[i]], vs[i])
+        err = np.abs(kn[i, :, pos[i]].astype(np.float64) - oracle.rope(ks[i], cos_t[i], sin_t[i]))
+        assert np.all(err <= _rope_row_bound(ks[i])), float(err.max())
+        keep = np.arange(ms) != pos[i]
+        assert np.all(kn[i][:, keep] == -2.0) and np.all(vn[i][:, keep] == 3.0)
