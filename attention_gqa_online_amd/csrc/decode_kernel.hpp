@@ -85,13 +85,18 @@ struct SeqRange {
     bool valid;
 };
 
-__device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, uint32_t b) {
-    if (a.lens == nullptr) return {a.w0, a.total_seq, a.position, true};
-    const uint64_t t = (uint64_t)a.lens[b] + a.len_add;
+// The same from sequence b's per-sequence length value `len` (lens[b]).
+__device__ __forceinline__ SeqRange seq_range_len(const DecodeArgs &a, uint32_t len) {
+    const uint64_t t = (uint64_t)len + a.len_add;
     const bool valid = t <= a.seq_bound;
     const uint32_t T = valid ? (uint32_t)t : 0;
     const uint32_t w0 = (a.window > 0 && T > a.window) ? T - a.window : 0;
     return {w0, T > 0 ? T - a.len_add : 0, T > 0 ? T - 1 : 0, valid};
+}
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeArgs &a, uint32_t b) {
+    if (a.lens == nullptr) return {a.w0, a.total_seq, a.position, true};
+    return seq_range_len(a, a.lens[b]);
 }
 
 // Rows of the split pass of unit u (per-sequence lengths).
@@ -149,6 +154,7 @@ __device__ __forceinline__ uint64_t prop_total(const DecodeArgs &a, int lane) {
 struct PropHit {
     uint32_t unit, first, n, rows;
     bool found;
+    uint32_t len;  // prop_locate: the unit's per-sequence length value
 };
 
 // The unit holding split index w (by_unit = false), or unit w itself
@@ -167,11 +173,42 @@ __device__ __forceinline__ PropHit prop_find(const DecodeArgs &a, uint64_t T, ui
         if (mask != 0) {
             const int src = __ffsll((long long)mask) - 1;
             return {(uint32_t)__shfl((int)u, src), (uint32_t)__shfl((int)S, src),
-                    (uint32_t)__shfl((int)ps.n, src), (uint32_t)__shfl((int)ps.rows, src), true};
+                    (uint32_t)__shfl((int)ps.n, src), (uint32_t)__shfl((int)ps.rows, src), true,
+                    0};
         }
         carry += (uint32_t)__shfl((int)incl, W - 1);
     }
-    return {0, 0, 0, 0, false};
+    return {0, 0, 0, 0, false, 0};
+}
+
+// prop_find with the batch total, and the found unit's length value. With
+// at most W units (the usual case) each lane loads its unit's length once and
+// the table is one scan: a single dependent global load before the split
+// pass can issue its first K/V loads.
+template <int W>
+__device__ __forceinline__ PropHit prop_locate(const DecodeArgs &a, uint32_t w, bool by_unit,
+                                               int lane) {
+    if (a.units > W) {
+        PropHit ph = prop_find<W>(a, prop_total<W>(a, lane), w, by_unit, lane);
+        if (ph.found) ph.len = a.lens[(ph.unit / a.n_chunks) / a.kv_heads];
+        return ph;
+    }
+    const uint32_t u = lane;
+    const bool in = u < a.units;
+    const uint32_t len = in ? a.lens[(u / a.n_chunks) / a.kv_heads] : 0;
+    const SeqRange r = seq_range_len(a, len);
+    const uint32_t L = in && r.hi > r.w0 ? r.hi - r.w0 : 0;
+    const uint64_t T = wave_sum_u64<W>(L);
+    const PropSplit ps = in ? prop_split(a, L, T) : PropSplit{0, 0};
+    const uint32_t incl = wave_incl_scan<W>(ps.n, lane);
+    const uint32_t S = incl - ps.n;
+    const bool hit = in && (by_unit ? u == w : (ps.n != 0 && S <= w && w - S < ps.n));
+    const unsigned long long mask = __ballot(hit);
+    if (mask == 0) return {0, 0, 0, 0, false, 0};
+    const int src = __ffsll((long long)mask) - 1;
+    return {(uint32_t)__shfl((int)u, src), (uint32_t)__shfl((int)S, src),
+            (uint32_t)__shfl((int)ps.n, src), (uint32_t)__shfl((int)ps.rows, src), true,
+            (uint32_t)__shfl((int)len, src)};
 }
 
 // What the split pass writes: one partial state per (unit, split, head) for
@@ -200,16 +237,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     uint32_t split = blockIdx.x % a.n_split;
     uint32_t unit = blockIdx.x / a.n_split;
     uint32_t rps = a.rows_per_split;
+    bool have_len = false;  // the unit's length value is already in `len`
+    uint32_t len = 0;
     if constexpr (MERGE == kMergePartialOnly) {
         if (a.lens != nullptr) {
             // per-sequence lengths: workgroup w is split w - first(u) of the
             // unit u whose splits include w (proportional table)
-            const uint64_t T = prop_total<64>(a, lane);
-            const PropHit ph = prop_find<64>(a, T, blockIdx.x, false, lane);
+            const PropHit ph = prop_locate<64>(a, blockIdx.x, false, lane);
             if (!ph.found) return;  // past the last split (uniform)
             unit = ph.unit;
             split = blockIdx.x - ph.first;
             rps = ph.rows;
+            len = ph.len;
+            have_len = true;
         }
     }
     const uint32_t chunk = unit % a.n_chunks;
@@ -222,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
     // rows of this workgroup, then of this wave: every NW-th step of the
     // workgroup's range, so the workgroup streams one contiguous region
-    const SeqRange sr = seq_range(a, b);
+    const SeqRange sr = have_len ? seq_range_len(a, len) : seq_range(a, b);
     const uint32_t ws0 = sr.w0 + split * rps;
     const uint32_t ws1 = min(ws0 + rps, sr.hi);
     const uint32_t ra = ws0 + wave * RPT;
@@ -505,21 +545,21 @@ __global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge
     const uint32_t hl0 = chunk * HC;
     if ((int)(a.hpk - hl0) <= hh) return;  // head past this chunk's end
     const uint32_t h = g * a.hpk + hl0 + hh;
-    const SeqRange sr = seq_range(a, b);
     uint32_t ns = a.n_split;
     size_t first = (size_t)unit * a.n_split;  // the unit's first split index
-    if (a.lens != nullptr) {
-        if (!sr.valid) {  // invalid length: NaN output, nothing appended
-            if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
-            return;
-        }
-        if (ns != 0) {  // the split pass ran with the proportional table
-            constexpr int W = NT < 64 ? NT : 64;
-            const int lane = threadIdx.x & 63;
-            const PropHit ph = prop_find<W>(a, prop_total<W>(a, lane), unit, true, lane);
-            first = ph.first;
-            ns = ph.n;
-        }
+    SeqRange sr;
+    if (a.lens != nullptr && ns != 0) {  // the split pass ran with the proportional table
+        constexpr int W = NT < 64 ? NT : 64;
+        const PropHit ph = prop_locate<W>(a, unit, true, (int)(threadIdx.x & 63));
+        first = ph.first;
+        ns = ph.n;
+        sr = seq_range_len(a, ph.len);
+    } else {
+        sr = seq_range(a, b);
+    }
+    if (!sr.valid) {  // invalid length: NaN output, nothing appended
+        if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
+        return;
     }
     constexpr uint32_t SS = HC * (D + 2);  // floats between splits
     const float *up = a.part + first * SS + hh * (D + 2);

@@ -1118,3 +1118,39 @@ def test_decode_rope_append_varlen_no_heads_rotates_each_row(dev):
         assert np.all(err <= _rope_row_bound(ks[i])), float(err.max())
         keep = np.arange(ms) != pos[i]
         assert np.all(kn[i][:, keep] == -2.0) and np.all(vn[i][:, keep] == 3.0)
+
+
+def test_decode_rope_append_varlen_invalid_position(dev):
+    """positions[b] + 1 > seq_bound: NaN output and no cache write for that
+    sequence; the others are the oracle's fused rotary step."""
+    b, hq, hkv, d, ms, bound = 3, 6, 2, 64, 32, 20
+    w = synth.DecodeWorkload("rv", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, seed=31)
+    q, k, v = synth.decode_inputs(w)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=32)
+    pos = np.array([19, 20, 4], np.uint32)
+    tabs = [synth.rope_tables(d, int(p)) for p in pos]
+    cos_t = np.ascontiguousarray(np.stack([t[0] for t in tabs]))
+    sin_t = np.ascontiguousarray(np.stack([t[1] for t in tabs]))
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    out = torch.zeros((b, hq, d), device=dev)
+    A.attn_decode_rope_append_varlen(
+        torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev),
+        torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev), kd, vd, out,
+        torch.from_numpy(pos.astype(np.int32)).to(dev), b, hq, hkv, d, ms, bound, 0, w.scale,
+        A.decode_workspace(b, hq, hkv, d, bound, 0))
+    torch.cuda.synchronize()
+    got, kc, vc = out.cpu().numpy(), kd.cpu().numpy(), vd.cpu().numpy()
+    assert np.all(np.isnan(got[1]))
+    assert np.array_equal(kc[1], k[1]) and np.array_equal(vc[1], v[1])
+    for i in (0, 2):
+        kr, vr = k[i:i + 1].copy(), v[i:i + 1].copy()
+        ref = oracle.decode_rope_append(q[i:i + 1], kn[i:i + 1], vn[i:i + 1], cos_t[i], sin_t[i],
+                                        kr, vr, 1, hq, hkv, d, ms, int(pos[i]), 0, w.scale)
+        assert np.array_equal(vc[i], vr[0])
+        keep = np.arange(ms) != pos[i]
+        assert np.array_equal(kc[i][:, keep], k[i][:, keep])
+        err = np.abs(kc[i, :, pos[i]].astype(np.float64) - kr[0, :, pos[i]])
+        assert np.all(err <= _rope_row_bound(kn[i])), float(err.max())
+        vmax = float(np.abs(vr[0, :, :pos[i] + 1]).max())  # rows the step attends
+        _assert_close(got[i:i + 1], ref, vmax, f"sequence {i}")
