@@ -315,14 +315,30 @@ def bench_decode_varlen(args, dev):
     med = statistics.median(ms)
     bytes_ = int(2 * w.kv_heads * w.head_dim * 4 * int(lens.astype(np.int64).sum()))
     gbs = bytes_ / (med * 1e-3) / 1e9
+
+    # the same step with rotary embedding, one cos/sin table per sequence
+    tabs = [synth.rope_tables(w.head_dim, int(p)) for p in lens - 1]
+    cos_t = torch.from_numpy(np.ascontiguousarray(np.stack([t[0] for t in tabs]))).to(dev)
+    sin_t = torch.from_numpy(np.ascontiguousarray(np.stack([t[1] for t in tabs]))).to(dev)
+
+    def rope_call(i):
+        q, k, v = sets[i % 3]
+        A.attn_decode_rope_append_varlen(q, kn, vn, cos_t, sin_t, k, v, out, pos, w.batch,
+                                         w.num_heads, w.kv_heads, w.head_dim, w.max_seq,
+                                         w.total_seq, w.window, w.scale, ws)
+    ms_r, _ = time_calls(rope_call, max(args.steps, 10), args.warmup, stream)
+    med_r = statistics.median(ms_r)
     del sets
     torch.cuda.empty_cache()
     log(f"[bench] varlen decode step: median {med * 1e3:.1f} us, {gbs:.0f} GB/s "
-        f"(mean length {lens.mean():.0f})")
+        f"(mean length {lens.mean():.0f}); rotary varlen step: median {med_r * 1e3:.1f} us")
     return {"workload": "decode_varlen_b32_hq12_hkv2_d128_t4096_uniform",
             "step": "attn_decode_append_varlen", "mean_len": round(float(lens.mean()), 1),
             "median_us": round(med * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
             "GB/s": round(gbs, 1),
+            "rope_step": {"step": "attn_decode_rope_append_varlen",
+                          "median_us": round(med_r * 1e3, 2),
+                          "GB/s": round(bytes_ / (med_r * 1e-3) / 1e9, 1)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("attn_decode_append_varlen")},

@@ -577,6 +577,7 @@ VARLEN_APPEND_CASES = [
     (4, 8, 8, 32, 40, 1, 0),             # bound 1: every sequence at position 0
     (64, 8, 4, 128, 200, 160, 0),
     (32, 12, 2, 128, 4096, 4096, 0),
+    (20, 4, 2, 32, 64, 64, 0),           # 40 units: more than one 32-lane merge wave's table
 ]
 
 
@@ -1055,7 +1056,8 @@ def test_decode_gqa_equals_mha_with_repeated_kv_heads(dev):
 
 
 @pytest.mark.parametrize("case", [(5, 12, 2, 128, 300, 300, 0), (4, 8, 8, 64, 90, 90, 17),
-                                  (3, 10, 2, 224, 200, 150, 0), (32, 12, 2, 128, 4096, 4096, 0)],
+                                  (3, 10, 2, 224, 200, 150, 0), (32, 12, 2, 128, 4096, 4096, 0),
+                                  (40, 8, 2, 64, 128, 128, 0)],
                          ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_bd{}_w{}".format(*c))
 def test_decode_rope_append_varlen_matches_oracle(dev, case):
     """Rotary decode step with one position and one angle table per sequence
