@@ -19,9 +19,15 @@ constexpr uint32_t kTargetWorkgroupsVarlen(uint32_t units) {
 }
 constexpr int kMinRowsPerWave = 32;
 
-// Lanes that hold one K/V row: 16, or 8 where a lane's share of the row
-// would not be whole float4 chunks (head_dim / 4 not a multiple of 16).
-constexpr int lanes_per_row(int d) { return (d / 4) % 16 == 0 ? 16 : 8; }
+// Lanes that hold one K/V row. Short rows (head_dim 32, 64) take d / 8
+// lanes, two float4 chunks each, as head_dim 128 does with 16: with one chunk
+// per lane the per-row work (the lane-group sum, exp, running sums) would be
+// paid for half the bytes and bound the loop by the vector ALU. Otherwise 16,
+// or 8 where a lane's share of the row would not be whole float4 chunks
+// (head_dim / 4 not a multiple of 16).
+constexpr int lanes_per_row(int d) {
+    return d == 32 ? 4 : d == 64 ? 8 : (d / 4) % 16 == 0 ? 16 : 8;
+}
 
 // Largest head chunk (at most 8) whose row-slot accumulators, [slots][HC][d]
 // floats, fit the 160 KiB of LDS next to the kernel's other arrays, and whose
