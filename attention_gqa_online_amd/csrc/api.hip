@@ -43,9 +43,10 @@ attn_status attn_prefill_causal(const float *q, const float *k, const float *v, 
     if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
     if (m == 0 || num_q_heads == 0) return ATTN_OK;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID;
-    // grid = kv_heads * ceil(heads_per_kv * ceil(m/32) / 8) workgroups
+    // grid = kv_heads * ceil(heads_per_kv * ceil(m/32) / waves) workgroups,
+    // waves 8 or 4
     const uint64_t pairs = (uint64_t)heads_per_kv * ((m + 31u) / 32u);
-    if (kv_heads * ((pairs + 7) / 8) > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if (kv_heads * ((pairs + 3) / 4) > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
     return from_hip(attn::launch_prefill(q, k, v, o, m, q_stride, kv_stride, num_q_heads,
                                          heads_per_kv, head_dim, stream));
 }

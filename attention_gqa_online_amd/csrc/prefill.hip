@@ -8,13 +8,15 @@
 //
 // MI355X design (the page's one-warp-per-head kernel with K/V through L2 is
 // prior art only):
-//   workgroup = 8 waves sharing one KV head g. Wave w of workgroup i owns the
-//               (row block, head) pair i*8 + w of the group, enumerated row
+//   workgroup = NW waves sharing one KV head g (NW = 8, or 4 for head_dim
+//               >= 192 on large grids: see kMinDim4Waves). Wave w of workgroup i owns the
+//               (row block, head) pair i*NW + w of the group, enumerated row
 //               block major, so the waves of a workgroup sit in at most a few
 //               consecutive 32-row blocks. Grids too small to fill the chip
-//               twice pair row blocks u and n-1-u instead (waves 0-3 / 4-7,
-//               four heads each), balancing the causal work per workgroup.
-//   K/V tiles of 64 keys are staged once in LDS and used by all 8 waves
+//               twice pair row blocks u and n-1-u instead (first / second
+//               half of the waves, NW/2 heads each), balancing the causal
+//               work per workgroup.
+//   K/V tiles of 64 keys are staged once in LDS and used by all the waves
 //   (every Q head of the group reads the same tile; the GQA reuse is explicit).
 //   Tiles go global -> LDS directly (no registers) into two buffers, so the
 //   next tile's loads run under the current tile's matrix work; one barrier
@@ -43,7 +45,13 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 8;
+// Waves per workgroup: 8 (two per SIMD, so one wave's softmax runs under the
+// other's matrix work), or, for head_dim >= 192 on grids that fill the chip
+// twice, 4: there Q^T and the O^T accumulators of a 32-row block alone take
+// head_dim registers, and with one wave per SIMD a lane has 512 registers
+// instead of 256, so nothing goes to scratch memory. (On smaller grids the
+// 4-wave workgroups would need two rounds of the CUs.)
+constexpr int kMinDim4Waves = 192;
 constexpr int kBr = 32;  // query rows per wave
 constexpr int kBc = 64;  // keys per LDS tile
 constexpr int kCus = 256;  // compute units of an MI355X
@@ -59,7 +67,7 @@ struct PrefillArgs {
     uint32_t wg_per_group; // workgroups per KV head
     uint32_t n_rb;         // ceil(m / 32)
     uint32_t zigzag;       // 1: waves 0-3 / 4-7 take row blocks u / n_rb-1-u
-    uint32_t nsub;         // zigzag: workgroups per row-block pair (ceil(hpk / 4))
+    uint32_t nsub;         // zigzag: workgroups per row-block pair (ceil(hpk / (waves / 2)))
     float qscale;          // (1/sqrt(d) in f32) * log2(e)
 };
 
@@ -85,12 +93,12 @@ __device__ __forceinline__ int swz_chunk(int row, int chunk) {
 // lanes x 16 bytes to consecutive LDS addresses; the lane picks which global
 // chunk fills its LDS slot, which is how the swizzle is applied. Rows past
 // m re-read row m - 1 (in bounds); the causal mask removes them.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void load_tile_lds(const PrefillArgs &a, uint32_t g, uint32_t kt,
                                               float *sk, float *sv, int wave, int lane) {
     constexpr int CPR = D / 4;                    // 16-byte chunks per row
-    constexpr int NI = kBc * CPR / (kWaves * 64); // instructions per wave per tensor
-    static_assert(NI >= 1 && kBc * CPR % (kWaves * 64) == 0, "tile split over waves");
+    constexpr int NI = kBc * CPR / (NW * 64);     // instructions per wave per tensor
+    static_assert(NI >= 1 && kBc * CPR % (NW * 64) == 0, "tile split over waves");
     // opaque copy of the lane id: the per-lane source offsets below are then
     // formed at each call instead of being hoisted out of the tile loop
     int ln = lane;
@@ -112,8 +120,9 @@ __device__ __forceinline__ void load_tile_lds(const PrefillArgs &a, uint32_t g, 
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+    constexpr int HW = NW / 2;  // zigzag: waves per row block of the pair
     constexpr int NQ = D / 8;   // float4 chunks of the Q^T operand per lane
     constexpr int NMD = D / 32; // 32-row blocks of O^T (= floats per lane per V row)
     constexpr int NBUF = D <= 128 ? 2 : 1;  // double-buffered tiles when LDS allows
@@ -136,22 +145,23 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     bool active;
     uint32_t rb, hl, rb_last;  // this wave's row block and head; the workgroup's last block
     if (a.zigzag) {
-        // small grids: waves 0-3 take heads of row block u, waves 4-7 the same
-        // heads of block n_rb-1-u, so each SIMD runs one short and one long
-        // wave and every workgroup has about the same work
+        // small grids: the first half of the waves take heads of row block
+        // u, the second half the same heads of block n_rb-1-u, so each SIMD
+        // runs one short and one long wave (8 waves) and every workgroup has
+        // about the same work
         const uint32_t u = wi / a.nsub;
-        hl = (wi % a.nsub) * 4 + (wave & 3);
+        hl = (wi % a.nsub) * HW + (wave % HW);
         const uint32_t lo = u, hi = a.n_rb - 1 - u;
-        rb = wave < 4 ? lo : hi;
-        active = hl < a.hpk && (wave < 4 || hi > lo);
+        rb = wave < HW ? lo : hi;
+        active = hl < a.hpk && (wave < HW || hi > lo);
         rb_last = hi;
     } else {
-        // row-block-major pairs: workgroup wi owns pairs wi*8 .. wi*8+7
-        const uint32_t pair = wi * kWaves + wave;
+        // row-block-major pairs: workgroup wi owns pairs wi*NW .. wi*NW+NW-1
+        const uint32_t pair = wi * NW + wave;
         active = pair < a.n_pairs;
         rb = pair / a.hpk;
         hl = pair % a.hpk;
-        rb_last = min(wi * kWaves + kWaves - 1, a.n_pairs - 1) / a.hpk;
+        rb_last = min(wi * NW + NW - 1, a.n_pairs - 1) / a.hpk;
     }
     const uint32_t h = g * a.hpk + (active ? hl : 0);
     const uint32_t qr0 = rb * kBr;
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     const uint32_t my_kend = active ? min(qr0 + kBr, a.m) : 0;
     const uint32_t my_ntiles = (my_kend + kBc - 1) / kBc;
 
-    load_tile_lds<D>(a, g, 0, sK0, sV0, wave, lane);
+    load_tile_lds<D, NW>(a, g, 0, sK0, sV0, wave, lane);
 
     // Q^T operand: lane (j, half) holds Q[qi][8u + 4half + 0..3] for u < D/8
     float4 qt[NQ];
@@ -331,12 +341,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
         for (uint32_t kt = 0; kt < ntiles; kt += 2) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
             __syncthreads();  // every wave's loads landed; buffer 1 is free
-            if (kt + 1 < ntiles) load_tile_lds<D>(a, g, kt + 1, sK1, sV1, wave, lane);
+            if (kt + 1 < ntiles) load_tile_lds<D, NW>(a, g, kt + 1, sK1, sV1, wave, lane);
             tile(sK0, sV0, kt);
             if (kt + 1 >= ntiles) break;
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();  // buffer 0 is free
-            if (kt + 2 < ntiles) load_tile_lds<D>(a, g, kt + 2, sK0, sV0, wave, lane);
+            if (kt + 2 < ntiles) load_tile_lds<D, NW>(a, g, kt + 2, sK0, sV0, wave, lane);
             tile(sK1, sV1, kt + 1);
         }
     } else {
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
             tile(sK0, sV0, kt);
             if (kt + 1 < ntiles) {
                 __syncthreads();  // single buffer: everyone done before it is refilled
-                load_tile_lds<D>(a, g, kt + 1, sK0, sV0, wave, lane);
+                load_tile_lds<D, NW>(a, g, kt + 1, sK0, sV0, wave, lane);
             }
         }
     }
@@ -366,8 +376,14 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(const PrefillArgs &args, uint32_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_kernel<D>), dim3(grid), dim3(kWaves * 64), 0, stream, args);
+hipError_t launch_d(const PrefillArgs &args, uint32_t grid, uint32_t nw, hipStream_t stream) {
+    if constexpr (D >= kMinDim4Waves) {
+        if (nw == 4) {
+            hipLaunchKernelGGL((prefill_kernel<D, 4>), dim3(grid), dim3(4 * 64), 0, stream, args);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((prefill_kernel<D, 8>), dim3(grid), dim3(8 * 64), 0, stream, args);
     return hipGetLastError();
 }
 
@@ -390,10 +406,13 @@ hipError_t launch_prefill(const float *q, const float *k, const float *v, float 
     const uint32_t n_rb = (m + kBr - 1) / kBr;
     a.n_rb = n_rb;
     a.n_pairs = heads_per_kv * n_rb;
-    a.wg_per_group = (a.n_pairs + kWaves - 1) / kWaves;
+    uint32_t nw = 8;
+    if (head_dim >= kMinDim4Waves && (uint64_t)(a.n_pairs + 3) / 4 * a.kv_heads >= 2 * kCus)
+        nw = 4;
+    a.wg_per_group = (a.n_pairs + nw - 1) / nw;
     // a grid under two workgroups per CU is bound by its heaviest workgroup:
     // pair short and long row blocks instead
-    a.nsub = (heads_per_kv + 3) / 4;
+    a.nsub = (heads_per_kv + nw / 2 - 1) / (nw / 2);
     if ((uint64_t)a.wg_per_group * a.kv_heads < 2 * kCus) {
         a.zigzag = 1;
         a.wg_per_group = (n_rb + 1) / 2 * a.nsub;
@@ -401,14 +420,14 @@ hipError_t launch_prefill(const float *q, const float *k, const float *v, float 
     a.qscale = (1.0f / sqrtf((float)head_dim)) * kLog2e;
     const uint32_t grid = a.wg_per_group * a.kv_heads;
     switch (head_dim) {
-    case 32: return launch_d<32>(a, grid, stream);
-    case 64: return launch_d<64>(a, grid, stream);
-    case 96: return launch_d<96>(a, grid, stream);
-    case 128: return launch_d<128>(a, grid, stream);
-    case 160: return launch_d<160>(a, grid, stream);
-    case 192: return launch_d<192>(a, grid, stream);
-    case 224: return launch_d<224>(a, grid, stream);
-    case 256: return launch_d<256>(a, grid, stream);
+    case 32: return launch_d<32>(a, grid, nw, stream);
+    case 64: return launch_d<64>(a, grid, nw, stream);
+    case 96: return launch_d<96>(a, grid, nw, stream);
+    case 128: return launch_d<128>(a, grid, nw, stream);
+    case 160: return launch_d<160>(a, grid, nw, stream);
+    case 192: return launch_d<192>(a, grid, nw, stream);
+    case 224: return launch_d<224>(a, grid, nw, stream);
+    case 256: return launch_d<256>(a, grid, nw, stream);
     default: return hipErrorInvalidValue;
     }
 }

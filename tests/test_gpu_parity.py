@@ -711,6 +711,23 @@ def test_prefill_row_block_major_path_ragged(dev):
     _assert_close(o[rows, heads], ref, _vmax_prefill(w, v), "row-block-major ragged")
 
 
+@pytest.mark.parametrize("d,m", [(192, 2040), (256, 2048)])
+def test_prefill_large_head_dim_four_wave_path(dev, d, m):
+    """head_dim >= 192 on a grid that fills the chip twice runs 4-wave
+    workgroups (one wave per SIMD); ragged last row block for d = 192.
+    Sample: the last 24 rows of every head plus 600 seeded random pairs."""
+    w = synth.PrefillWorkload("case", m=m, num_q_heads=32, heads_per_kv=4, head_dim=d,
+                              q_stride=32 * d, kv_stride=8 * d, seed=d + m)
+    q, k, v = synth.prefill_inputs(w)
+    o = _heads(w, _gpu_prefill(dev, w, q, k, v))
+    rng = np.random.default_rng(d)
+    rows = [np.repeat(np.arange(w.m - 24, w.m), 32), rng.integers(0, w.m, 600)]
+    heads = [np.tile(np.arange(32), 24), rng.integers(0, 32, 600)]
+    rows, heads = np.concatenate(rows), np.concatenate(heads)
+    ref = _ref_prefill(w, q, k, v, rows=rows, heads=heads)
+    _assert_close(o[rows, heads], ref, _vmax_prefill(w, v), f"d {d} m {m}")
+
+
 PREFILL_SWEEP = [
     # (m, hq, hpk, d)
     (1, 1, 1, 32), (2, 2, 1, 64), (15, 4, 2, 32), (16, 4, 2, 32), (17, 4, 2, 32),
