@@ -54,8 +54,12 @@ template <int D, int HC>
 hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStream_t stream) {
     constexpr int LPR = lanes_per_row(D);
     if (n_split == 1 && args.k_new == nullptr) {
-        hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeDirect>),
-                           dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
+        if (args.lens != nullptr)
+            hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeDirect, true>),
+                               dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
+        else
+            hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeDirect, false>),
+                               dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
         return hipGetLastError();
     }
     uint32_t grid = units * n_split;
@@ -69,8 +73,12 @@ hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStrea
         grid = args.g_target + units;
     }
     if (n_split > 0) {
-        hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly>),
-                           dim3(grid), dim3(kDecodeWaves * 64), 0, stream, args);
+        if (args.lens != nullptr)
+            hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly, true>),
+                               dim3(grid), dim3(kDecodeWaves * 64), 0, stream, args);
+        else
+            hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly, false>),
+                               dim3(grid), dim3(kDecodeWaves * 64), 0, stream, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

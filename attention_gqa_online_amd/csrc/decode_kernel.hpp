@@ -215,7 +215,9 @@ __device__ __forceinline__ PropHit prop_locate(const DecodeArgs &a, uint32_t w, 
 // the merge kernel, or, with a single split per unit, the normalised output.
 enum DecodeMerge { kMergePartialOnly = 1, kMergeDirect = 3 };
 
-template <int D, int HC, int LPR, int NW, int P, int MERGE>
+// VARLEN: per-sequence lengths (a.lens set); without, the code for them is not
+// compiled in, so the uniform kernel carries none of its registers.
+template <int D, int HC, int LPR, int NW, int P, int MERGE, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     constexpr int VPL = D / LPR;   // floats per lane per row
     constexpr int NF4 = VPL / 4;   // float4 per lane per row
@@ -239,8 +241,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     uint32_t rps = a.rows_per_split;
     bool have_len = false;  // the unit's length value is already in `len`
     uint32_t len = 0;
-    if constexpr (MERGE == kMergePartialOnly) {
-        if (a.lens != nullptr) {
+    if constexpr (MERGE == kMergePartialOnly && VARLEN) {
+        {
             // per-sequence lengths: workgroup w is split w - first(u) of the
             // unit u whose splits include w (proportional table)
             const PropHit ph = prop_locate<64>(a, blockIdx.x, false, lane);
@@ -262,7 +264,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
     // rows of this workgroup, then of this wave: every NW-th step of the
     // workgroup's range, so the workgroup streams one contiguous region
-    const SeqRange sr = have_len ? seq_range_len(a, len) : seq_range(a, b);
+    const SeqRange sr = !VARLEN ? SeqRange{a.w0, a.total_seq, a.position, true}
+                        : have_len ? seq_range_len(a, len)
+                                   : seq_range(a, b);
     const uint32_t ws0 = sr.w0 + split * rps;
     const uint32_t ws1 = min(ws0 + rps, sr.hi);
     const uint32_t ra = ws0 + wave * RPT;
