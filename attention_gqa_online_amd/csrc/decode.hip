@@ -163,7 +163,7 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     const size_t slots = varlen && !(p.n_split == 1 && !append)
                              ? (size_t)kTargetWorkgroupsVarlen(p.units) + p.units
                              : (size_t)p.units * p.n_split;
-    p.part_floats = slots * p.head_chunk * (head_dim + 2);
+    p.part_floats = slots * p.head_chunk * (head_dim + 4);  // kPartStride
     p.workspace_bytes = p.part_floats * sizeof(float);
     return p;
 }

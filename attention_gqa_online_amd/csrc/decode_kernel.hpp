@@ -50,7 +50,7 @@ struct DecodeArgs {
     const float *k;
     const float *v;
     float *out;
-    float *part;      // [splits][HC][D + 2]: acc[D], m, l; splits numbered unit by unit
+    float *part;      // [splits][HC][D + 4]: acc[D], m, l, 2 pad; splits numbered unit by unit
     // fused append (merge kernel only): new rows [B, Hkv, D], or null
     const float *k_new;
     const float *v_new;
@@ -211,6 +211,11 @@ __device__ __forceinline__ PropHit prop_locate(const DecodeArgs &a, uint32_t w, 
             (uint32_t)__shfl((int)len, src)};
 }
 
+// Floats per (split, head) partial state: acc[D], m, l and two floats of
+// padding, so every state starts on a 16-byte boundary (float4 stores).
+template <int D>
+constexpr int kPartStride = D + 4;
+
 // What the split pass writes: one partial state per (unit, split, head) for
 // the merge kernel, or, with a single split per unit, the normalised output.
 enum DecodeMerge { kMergePartialOnly = 1, kMergeDirect = 3 };
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     constexpr int NSLOT = NW * RPT;
     static_assert(VPL % 4 == 0 && LPR * VPL == D, "lane tiling");
 
-    __shared__ float s_acc[NSLOT][HC][D];  // per row slot partial accumulators
+    __shared__ __attribute__((aligned(16))) float s_acc[NSLOT][HC][D];  // per row slot accumulators
     __shared__ float s_l[NSLOT][HC];
     __shared__ float s_wm[NW][HC];         // per wave maximum reference
 
@@ -479,28 +484,43 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // this workgroup's partial state per head: (acc[d], M, L)
-    float *mypart = a.part + (size_t)blockIdx.x * HC * (D + 2);  // split index = workgroup
-    for (int idx = tid; idx < HC * D; idx += NW * 64) {
-        const int hh = idx / D;
-        const int d = idx % D;
-        float x = 0.f;
-#pragma unroll 8
-        for (int sl = 0; sl < NSLOT; ++sl) x += s_acc[sl][hh][d];
+    // this workgroup's partial state per head: (acc[d], M, L); a thread sums
+    // four consecutive d over all slots, every slot's LDS read issued at once
+    float *mypart = a.part + (size_t)blockIdx.x * HC * kPartStride<D>;  // split index = workgroup
+    for (int v = tid; v < HC * D / 4; v += NW * 64) {
+        const int hh = v / (D / 4);
+        const int d = 4 * (v % (D / 4));
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) {
+            const float4 y = ld4(&s_acc[sl][hh][d]);
+            x.x += y.x;
+            x.y += y.y;
+            x.z += y.z;
+            x.w += y.w;
+        }
         float lsum = 0.f;
-        if (d == 0 || MERGE == kMergeDirect)
+        if (d == 0 || MERGE == kMergeDirect) {
+#pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh];
+        }
         if constexpr (MERGE == kMergeDirect) {
             // no rows (an idle sequence): 0; an invalid length: NaN
-            const float o = !sr.valid ? __builtin_nanf("") : lsum > 0.f ? x / lsum : 0.f;
-            if (hh < nh) a.out[((size_t)b * a.num_heads + h0 + hh) * D + d] = o;
+            const bool nan = !sr.valid, zero = !(lsum > 0.f);
+            float4 o;
+            o.x = nan ? __builtin_nanf("") : zero ? 0.f : x.x / lsum;
+            o.y = nan ? __builtin_nanf("") : zero ? 0.f : x.y / lsum;
+            o.z = nan ? __builtin_nanf("") : zero ? 0.f : x.z / lsum;
+            o.w = nan ? __builtin_nanf("") : zero ? 0.f : x.w / lsum;
+            if (hh < nh) st4(a.out + ((size_t)b * a.num_heads + h0 + hh) * D + d, o);
         } else {
-            mypart[hh * (D + 2) + d] = x;
+            float *ph = mypart + hh * kPartStride<D>;
+            st4(ph + d, x);
             if (d == 0) {
                 float M = s_wm[0][hh];
                 for (int w2 = 1; w2 < NW; ++w2) M = fmaxf(M, s_wm[w2][hh]);
-                mypart[hh * (D + 2) + D] = M;
-                mypart[hh * (D + 2) + D + 1] = lsum;
+                ph[D] = M;
+                ph[D + 1] = lsum;
             }
         }
     }
@@ -565,8 +585,8 @@ __global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge
         if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
         return;
     }
-    constexpr uint32_t SS = HC * (D + 2);  // floats between splits
-    const float *up = a.part + first * SS + hh * (D + 2);
+    constexpr uint32_t SS = HC * kPartStride<D>;  // floats between splits
+    const float *up = a.part + first * SS + hh * kPartStride<D>;
 
     // partial states are read eight splits per round (independent loads);
     // a round's entries past ns re-read the last split with weight 0
