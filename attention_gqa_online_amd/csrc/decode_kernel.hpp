@@ -231,8 +231,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     static_assert(VPL % 4 == 0 && LPR * VPL == D, "lane tiling");
 
     __shared__ __attribute__((aligned(16))) float s_acc[NSLOT][HC][D];  // per row slot accumulators
-    __shared__ float s_l[NSLOT][HC];
-    __shared__ float s_wm[NW][HC];         // per wave maximum reference
+    __shared__ float s_m[HC][NSLOT];       // per row slot reference m and sum l
+    __shared__ float s_l[HC][NSLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -450,59 +450,48 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
     }
 
-    // The row slots merge against the workgroup's per-head maximum reference
-    // M: the maximum over a wave's slots comes from lane shuffles, over the
-    // waves from LDS; each slot then scales its own state by 2^(m - M)
-    // before it lands in LDS, so the final sum is a plain one.
-    {
-        float x[HC];
-#pragma unroll
-        for (int hh = 0; hh < HC; ++hh) x[hh] = m[hh];
-#pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) {  // stage-major: one round trip per stage
-            float y[HC];
-#pragma unroll
-            for (int hh = 0; hh < HC; ++hh) y[hh] = __shfl_xor(x[hh], o);
-#pragma unroll
-            for (int hh = 0; hh < HC; ++hh) x[hh] = fmaxf(x[hh], y[hh]);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int hh = 0; hh < HC; ++hh) s_wm[wave][hh] = x[hh];
-        }
-    }
-    __syncthreads();
+    // The row slots merge in LDS with one barrier: every slot stores its
+    // state (acc, m, l) as it is; a thread then takes the per-head maximum M
+    // of the slots' m and sums 2^(m - M) acc over the slots, four consecutive
+    // d at a time, with every LDS read in flight at once.
 #pragma unroll
     for (int hh = 0; hh < HC; ++hh) {
-        float M = s_wm[0][hh];
 #pragma unroll
-        for (int w2 = 1; w2 < NW; ++w2) M = fmaxf(M, s_wm[w2][hh]);
-        const float f = fast_exp2(m[hh] - M);  // m, M >= kMinRef: finite, no NaN
-#pragma unroll
-        for (int t = 0; t < NF4; ++t) st4(&s_acc[slot][hh][4 * (c + LPR * t)], acc[hh][t] * f);
-        if (c == 0) s_l[slot][hh] = l[hh] * f;
+        for (int t = 0; t < NF4; ++t) st4(&s_acc[slot][hh][4 * (c + LPR * t)], acc[hh][t]);
+        if (c == 0) {
+            s_m[hh][slot] = m[hh];
+            s_l[hh][slot] = l[hh];
+        }
     }
     __syncthreads();
 
-    // this workgroup's partial state per head: (acc[d], M, L); a thread sums
-    // four consecutive d over all slots, every slot's LDS read issued at once
+    // this workgroup's partial state per head: (acc[d], M, L)
     float *mypart = a.part + (size_t)blockIdx.x * HC * kPartStride<D>;  // split index = workgroup
     for (int v = tid; v < HC * D / 4; v += NW * 64) {
         const int hh = v / (D / 4);
         const int d = 4 * (v % (D / 4));
+        float ws[NSLOT];
+        float M = kNegInf;
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) {
+            ws[sl] = s_m[hh][sl];
+            M = fmaxf(M, ws[sl]);
+        }
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) ws[sl] = fast_exp2(ws[sl] - M);  // m, M >= kMinRef: no NaN
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl) {
             const float4 y = ld4(&s_acc[sl][hh][d]);
-            x.x += y.x;
-            x.y += y.y;
-            x.z += y.z;
-            x.w += y.w;
+            x.x += ws[sl] * y.x;
+            x.y += ws[sl] * y.y;
+            x.z += ws[sl] * y.z;
+            x.w += ws[sl] * y.w;
         }
         float lsum = 0.f;
         if (d == 0 || MERGE == kMergeDirect) {
 #pragma unroll
-            for (int sl = 0; sl < NSLOT; ++sl) lsum += s_l[sl][hh];
+            for (int sl = 0; sl < NSLOT; ++sl) lsum += ws[sl] * s_l[hh][sl];
         }
         if constexpr (MERGE == kMergeDirect) {
             // no rows (an idle sequence): 0; an invalid length: NaN
@@ -517,8 +506,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             float *ph = mypart + hh * kPartStride<D>;
             st4(ph + d, x);
             if (d == 0) {
-                float M = s_wm[0][hh];
-                for (int w2 = 1; w2 < NW; ++w2) M = fmaxf(M, s_wm[w2][hh]);
                 ph[D] = M;
                 ph[D + 1] = lsum;
             }
