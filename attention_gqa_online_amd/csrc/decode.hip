@@ -53,6 +53,7 @@ constexpr int merge_threads(int d) { return d <= 64 ? d : (d + 63) / 64 * 64; }
 template <int D, int HC>
 hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStream_t stream) {
     constexpr int LPR = lanes_per_row(D);
+    args.units = units;
     if (n_split == 1 && args.k_new == nullptr) {
         if (args.lens != nullptr)
             hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeDirect, true>),

@@ -50,7 +50,8 @@ struct DecodeArgs {
     const float *k;
     const float *v;
     float *out;
-    float *part;      // [splits][HC][D + 4]: acc[D], m, l, 2 pad; splits numbered unit by unit
+    float *part;      // [splits][HC][D + 4]: acc[D], m, l, 2 pad; split s of unit u at s * units + u
+                      // (per-sequence lengths: proportional splits numbered unit by unit)
     // fused append (merge kernel only): new rows [B, Hkv, D], or null
     const float *k_new;
     const float *v_new;
@@ -241,8 +242,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const int c = lane % LPR;
     const int slot = wave * RPT + r;
 
-    uint32_t split = blockIdx.x % a.n_split;
-    uint32_t unit = blockIdx.x / a.n_split;
+    // split-major numbering: the splits of a unit are units apart, so with
+    // units a multiple of 8 they land on one XCD (workgroups go round-robin
+    // over the 8 XCDs), and so does the unit's merge workgroup
+    uint32_t split = blockIdx.x / a.units;
+    uint32_t unit = blockIdx.x % a.units;
     uint32_t rps = a.rows_per_split;
     bool have_len = false;  // the unit's length value is already in `len`
     uint32_t len = 0;
@@ -547,8 +551,8 @@ __global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge
     constexpr int NT = D <= 64 ? D : (D + 63) / 64 * 64;
     const bool live = (int)threadIdx.x < D;
     const int tid = live ? (int)threadIdx.x : D - 1;
-    const uint32_t unit = blockIdx.x / HC;
-    const int hh = blockIdx.x % HC;
+    const uint32_t unit = blockIdx.x % a.units;
+    const int hh = blockIdx.x / a.units;
     const uint32_t chunk = unit % a.n_chunks;
     const uint32_t bg = unit / a.n_chunks;
     const uint32_t g = bg % a.kv_heads;
@@ -557,12 +561,14 @@ __global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge
     if ((int)(a.hpk - hl0) <= hh) return;  // head past this chunk's end
     const uint32_t h = g * a.hpk + hl0 + hh;
     uint32_t ns = a.n_split;
-    size_t first = (size_t)unit * a.n_split;  // the unit's first split index
+    size_t first = unit;  // the unit's first split index
+    size_t sstride = (size_t)a.units;  // split indices between its splits
     SeqRange sr;
     if (a.lens != nullptr && ns != 0) {  // the split pass ran with the proportional table
         constexpr int W = NT < 64 ? NT : 64;
         const PropHit ph = prop_locate<W>(a, unit, true, (int)(threadIdx.x & 63));
         first = ph.first;
+        sstride = 1;
         ns = ph.n;
         sr = seq_range_len(a, ph.len);
     } else {
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t sp = min(s0 + i, ns - 1);
-            const float *ps = up + (size_t)sp * SS;
+            const float *ps = up + (size_t)sp * sstride * SS;
             ms[i] = s0 + i < ns ? ps[D] : kNegInf;
             ls[i] = ps[D + 1];
             xs[i] = ps[tid];
