@@ -183,14 +183,15 @@ def attn_decode_workspace_bytes(batch, num_heads, kv_heads, head_dim,
 
 def decode_workspace(batch, num_heads, kv_heads, head_dim, total_seq, window,
                      device=None):
-    """A uint8 workspace tensor sized for these decode shapes (no clearing
-    needed: attn_decode overwrites what it reads)."""
+    """A zero-filled uint8 workspace tensor sized for these decode shapes
+    (the arrival counters at its start must be zero before the first call;
+    every call leaves them at zero)."""
     import torch
     n = attn_decode_workspace_bytes(batch, num_heads, kv_heads, head_dim,
                                     total_seq, window)
     if n == 0:
         raise ValueError("invalid decode shapes")
-    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
 
 
 def attn_decode(q, k_cache, v_cache, out, batch, num_heads, kv_heads, head_dim,

@@ -18,6 +18,7 @@ constexpr uint32_t kTargetWorkgroupsVarlen(uint32_t units) {
     return units / 2 + 64 < (uint32_t)kTargetWorkgroups ? kTargetWorkgroups - units / 2 : 64;
 }
 constexpr int kMinRowsPerWave = 32;
+constexpr size_t kCounterBlock = 65536;  // bytes of arrival counters: 16384 units
 
 // Lanes that hold one K/V row. Short rows (head_dim 32, 64) take d / 8
 // lanes, two float4 chunks each, as head_dim 128 does with 16: with one chunk
@@ -46,10 +47,13 @@ constexpr int max_head_chunk(int d) {
 // Threads of a merge workgroup: one per d, rounded up to whole waves.
 constexpr int merge_threads(int d) { return d <= 64 ? d : (d + 63) / 64 * 64; }
 
-// Pass 1 writes one partial state per (unit, split, head); pass 2, ordered
-// after it on the same stream, merges the splits of every (unit, head). With
-// a single split per unit and no appended row, pass 1 writes the normalised
-// output itself.
+// Uniform lengths: one launch. With a single split per unit and no appended
+// row it writes the normalised output itself; otherwise the last workgroup
+// of each unit merges the splits' partial states (kMergeFused). With no row
+// before the appended one (n_split 0) only the merge kernel runs.
+// Per-sequence lengths: pass 1 writes one partial state per (unit, split,
+// head); pass 2, ordered after it on the same stream, merges the splits of
+// every (unit, head).
 template <int D, int HC>
 hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStream_t stream) {
     constexpr int LPR = lanes_per_row(D);
@@ -63,23 +67,19 @@ hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStrea
                                dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
         return hipGetLastError();
     }
-    uint32_t grid = units * n_split;
-    if (args.lens != nullptr) {
+    if (args.lens == nullptr && n_split > 0) {
+        hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeFused, false>),
+                           dim3(units * n_split), dim3(kDecodeWaves * 64), 0, stream, args);
+        return hipGetLastError();
+    }
+    if (n_split > 0) {
         // proportional splits: at most g_target + units of them hold rows;
         // the workgroups past the last one exit at once
-        args.units = units;
         args.g_target = kTargetWorkgroupsVarlen(units);
         args.min_rows = kDecodeWaves * kMinRowsPerWave;
         args.rows_step = kDecodeWaves * (64 / LPR);
-        grid = args.g_target + units;
-    }
-    if (n_split > 0) {
-        if (args.lens != nullptr)
-            hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly, true>),
-                               dim3(grid), dim3(kDecodeWaves * 64), 0, stream, args);
-        else
-            hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly, false>),
-                               dim3(grid), dim3(kDecodeWaves * 64), 0, stream, args);
+        hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly, true>),
+                           dim3(args.g_target + units), dim3(kDecodeWaves * 64), 0, stream, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -165,7 +165,14 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
                              ? (size_t)kTargetWorkgroupsVarlen(p.units) + p.units
                              : (size_t)p.units * p.n_split;
     p.part_floats = slots * p.head_chunk * (head_dim + 4);  // kPartStride
-    p.workspace_bytes = p.part_floats * sizeof(float);
+    // arrival counters of the fused merge first (one per unit), then the
+    // partial states. The counter block has one size for every shape up to
+    // kCounterBlock / 4 units, so calls of different shapes can share a
+    // workspace without one call's partial states landing on another's
+    // counters.
+    const size_t cnt_bytes = ((size_t)p.units * sizeof(uint32_t) + 255) / 256 * 256;
+    p.part_offset = cnt_bytes > kCounterBlock ? cnt_bytes : kCounterBlock;
+    p.workspace_bytes = p.part_offset + p.part_floats * sizeof(float);
     return p;
 }
 
@@ -180,7 +187,8 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
     a.k = k_cache;
     a.v = v_cache;
     a.out = out;
-    a.part = static_cast<float *>(workspace);
+    a.cnt = static_cast<uint32_t *>(workspace);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.part_offset);
     a.num_heads = num_heads;
     a.kv_heads = kv_heads;
     a.hpk = num_heads / kv_heads;

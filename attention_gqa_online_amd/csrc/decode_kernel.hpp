@@ -28,14 +28,16 @@
 // score, and the rare wave whose scores climb more than kMaxHeadroom above m
 // re-streams its rows once with m = that maximum.
 // The row slots and waves of a workgroup merge through LDS into one partial
-// state (m, l, acc[d]) per head, written to the workspace; a second kernel
-// on the same stream folds the partial states of every (unit, head) with a
-// running log-sum-exp and writes the normalised output. When the call also
-// appends the current token (attn_decode_append), the split pass covers the
-// rows before it and the merge kernel folds the new row in as one more
-// partial state, scored from the new K row itself, and writes the new K and
-// V rows into the caches (rotated first when the call applies rotary
-// embedding; the split pass then rotates q as it loads it).
+// state (m, l, acc[d]) per head, written to the workspace; the last
+// workgroup of each unit to finish (an arrival counter per unit) folds the
+// partial states of its heads with a running log-sum-exp and writes the
+// normalised output (decode_fused_merge). With per-sequence lengths a second
+// kernel on the same stream does that fold instead (decode_merge_kernel).
+// When the call also appends the current token (attn_decode_append), the
+// split pass covers the rows before it and the merge folds the new row in as
+// one more partial state, scored from the new K row itself, and writes the
+// new K and V rows into the caches (rotated first when the call applies
+// rotary embedding; the split pass then rotates q as it loads it).
 #pragma once
 
 #include "common.hpp"
@@ -50,6 +52,7 @@ struct DecodeArgs {
     const float *k;
     const float *v;
     float *out;
+    uint32_t *cnt;    // [units] arrival counters of the fused merge: zero between calls
     float *part;      // [splits][HC][D + 4]: acc[D], m, l, 2 pad; split s of unit u at s * units + u
                       // (per-sequence lengths: proportional splits numbered unit by unit)
     // fused append (merge kernel only): new rows [B, Hkv, D], or null
@@ -219,7 +222,216 @@ constexpr int kPartStride = D + 4;
 
 // What the split pass writes: one partial state per (unit, split, head) for
 // the merge kernel, or, with a single split per unit, the normalised output.
-enum DecodeMerge { kMergePartialOnly = 1, kMergeDirect = 3 };
+// kMergeFused: the split pass also merges: the last workgroup of a unit to
+// finish folds every split's state (and the appended row) and writes out.
+enum DecodeMerge { kMergePartialOnly = 1, kMergeFused = 2, kMergeDirect = 3 };
+
+// Partial states that another workgroup of the same launch reads back go
+// through agent-scope (relaxed) atomic stores and loads, 8 bytes each: these
+// carry the device-scope cache bit (sc1), so a store is written through the
+// XCD's own L2 and acknowledged once every XCD can see it, and a load does
+// not take a line another XCD may have changed. No L2-wide writeback or
+// invalidate (what an agent-scope release/acquire fence costs) is needed.
+__device__ __forceinline__ void st_dev2(float *p, float x, float y) {
+    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) |
+                       ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float *p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__builtin_bit_cast(float, (uint32_t)v),
+                       __builtin_bit_cast(float, (uint32_t)(v >> 32)));
+}
+
+// Merge of the split pass (kMergeFused), run by every workgroup after its
+// slot merge. Each workgroup holds its own partial state in registers, one
+// (head, 4 consecutive d) item per thread (two for the largest head chunks).
+// With several splits per unit it stores that state, waits until the stores
+// are acknowledged, and one thread counts the split in on the unit's
+// arrival counter; the workgroup that brings the count to n_split is the
+// last and the only one to go on (it also returns the counter to 0 for the
+// next call). That workgroup folds, with a running log-sum-exp (M, num, den)
+// per item: the appended row (state m = its score, l = 1, acc = v_new; the
+// score is summed over the items of a head in LDS), then every split's state
+// in index order, and writes acc / l. It also writes the new K and V rows
+// into the caches (chunk 0 of each KV head).
+template <int D, int HC, int NW, typename SlotMerge>
+__device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerge &slot_merge,
+                                                   int tid, uint32_t unit, uint32_t split,
+                                                   uint32_t b, uint32_t bg, uint32_t h0,
+                                                   uint32_t hl0, int nh) {
+    constexpr int NT = NW * 64;
+    constexpr int NV = HC * D / 4;  // items
+    constexpr int NITEM = (NV + NT - 1) / NT;
+    constexpr int PS = kPartStride<D>;
+    __shared__ __attribute__((aligned(16))) float s_dot[HC][D / 4];
+    __shared__ uint32_t s_last;
+
+    // item it of this thread; threads past NV repeat the last item and
+    // store nothing
+    int hv[NITEM], dv[NITEM];
+    bool own[NITEM];
+    float4 num[NITEM];
+    float M[NITEM], den[NITEM];
+#pragma unroll
+    for (int it = 0; it < NITEM; ++it) {
+        const int v0 = tid + it * NT;
+        own[it] = v0 < NV;
+        const int v = own[it] ? v0 : NV - 1;
+        hv[it] = v / (D / 4);
+        dv[it] = 4 * (v % (D / 4));
+        slot_merge(v, num[it], M[it], den[it], true);
+    }
+
+    const uint32_t ns = a.n_split;
+    if (ns > 1) {
+        float *mypart = a.part + (size_t)blockIdx.x * HC * PS;  // split index = workgroup
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+            if (!own[it]) continue;
+            float *ph = mypart + hv[it] * PS;
+            st_dev2(ph + dv[it], num[it].x, num[it].y);
+            st_dev2(ph + dv[it] + 2, num[it].z, num[it].w);
+            if (dv[it] == 0) st_dev2(ph + D, M[it], den[it]);
+        }
+        // every thread's stores are acknowledged before the barrier, and the
+        // count goes up only after it
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t prev =
+                __hip_atomic_fetch_add(a.cnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = prev == ns - 1;
+            if (last) __hip_atomic_store(a.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last ? 1u : 0u;
+        }
+        __syncthreads();
+        if (s_last == 0) return;
+    }
+
+    // Fold in a fixed order, whichever workgroup merges (run-to-run
+    // deterministic): the appended row first, then the splits by index, all
+    // read back from the workspace (this workgroup's own state too), eight
+    // per round as independent loads; entries of a round past ns re-read the
+    // last split with weight 0. With a single split its state is still in
+    // registers.
+    float4 xo[NITEM];
+    float Mo[NITEM], Lo[NITEM];
+#pragma unroll
+    for (int it = 0; it < NITEM; ++it) {
+        xo[it] = num[it];
+        Mo[it] = M[it];
+        Lo[it] = den[it];
+        num[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        M[it] = kNegInf;
+        den[it] = 0.f;
+    }
+    float2 ml[NITEM][8];
+    float4 xs[NITEM][8];
+    auto load_round = [&](uint32_t s0) {
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t sp = min(s0 + i, ns - 1);
+                const float *ps =
+                    a.part + ((size_t)sp * a.units + unit) * HC * PS + hv[it] * PS;
+                ml[it][i] = ld_dev2(ps + D);
+                const float2 lo = ld_dev2(ps + dv[it]);
+                const float2 hi = ld_dev2(ps + dv[it] + 2);
+                xs[it][i] = make_float4(lo.x, lo.y, hi.x, hi.y);
+                if (s0 + i >= ns) ml[it][i].x = kNegInf;
+            }
+        }
+    };
+    auto fold_round = [&](int n) {
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+            float Mn = M[it];
+            for (int i = 0; i < n; ++i) Mn = fmaxf(Mn, ml[it][i].x);
+            const float c = M[it] == kNegInf ? 0.f : fast_exp2(M[it] - Mn);
+            num[it] = num[it] * c;
+            den[it] *= c;
+            for (int i = 0; i < n; ++i) {
+                const float w = ml[it][i].x == kNegInf ? 0.f : fast_exp2(ml[it][i].x - Mn);
+                num[it].x += xs[it][i].x * w;
+                num[it].y += xs[it][i].y * w;
+                num[it].z += xs[it][i].z * w;
+                num[it].w += xs[it][i].w * w;
+                den[it] += ml[it][i].y * w;
+            }
+            M[it] = Mn;
+        }
+    };
+    if (ns > 1) load_round(0);  // in flight while the new row is scored
+
+    if (a.k_new != nullptr) {
+        float4 kn[NITEM], vn[NITEM];
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+            const int hh = hv[it], d = dv[it];
+            const int hq = hh < nh ? hh : nh - 1;  // heads past nh: in bounds, never stored
+            const float *qp = a.q + ((size_t)b * a.num_heads + h0 + hq) * D + d;
+            const float *kp = a.k_new + (size_t)bg * D + d;
+            float4 qd = ld4(qp);
+            kn[it] = ld4(kp);
+            vn[it] = ld4(a.v_new + (size_t)bg * D + d);
+            if (a.cos_t != nullptr) {  // rotate-half: q and the new K row
+                const bool lo = d < D / 2;
+                const int off = lo ? D / 2 : -D / 2;
+                const size_t ci = (size_t)b * a.cs_stride + (d % (D / 2));
+                const float4 cc = ld4(a.cos_t + ci);
+                const float4 ss = ld4(a.sin_t + ci);
+                kn[it] = rope_half(kn[it], ld4(kp + off), cc, ss, lo);
+                qd = rope_half(qd, ld4(qp + off), cc, ss, lo);
+            }
+            if (own[it]) s_dot[hh][d / 4] = dot4(qd * a.qscale, kn[it]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+            // the new row's state: m = its score (log2 units), l = 1, acc = v_new
+            float sc = 0.f;
+#pragma unroll
+            for (int j = 0; j < D / 4; j += 4) {
+                const float4 y = ld4(&s_dot[hv[it]][j]);
+                sc += (y.x + y.y) + (y.z + y.w);
+            }
+            M[it] = sc;
+            num[it] = vn[it];
+            den[it] = 1.f;
+            if (hl0 == 0 && hv[it] == 0 && own[it]) {  // one writer per (sequence, KV head)
+                const size_t dst = ((size_t)bg * a.max_seq + a.position) * D + dv[it];
+                st4(a.k_dst + dst, kn[it]);
+                st4(a.v_dst + dst, vn[it]);
+            }
+        }
+    }
+
+    if (ns > 1) {
+        fold_round(8);
+        for (uint32_t s0 = 8; s0 < ns; s0 += 8) {
+            load_round(s0);
+            fold_round(8);
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+            ml[it][0] = make_float2(Mo[it], Lo[it]);
+            xs[it][0] = xo[it];
+        }
+        fold_round(1);
+    }
+#pragma unroll
+    for (int it = 0; it < NITEM; ++it) {
+        if (!own[it] || hv[it] >= nh) continue;
+        const float4 o = make_float4(num[it].x / den[it], num[it].y / den[it],
+                                     num[it].z / den[it], num[it].w / den[it]);
+        st4(a.out + ((size_t)b * a.num_heads + h0 + hv[it]) * D + dv[it], o);
+    }
+}
 
 // VARLEN: per-sequence lengths (a.lens set); without, the code for them is not
 // compiled in, so the uniform kernel carries none of its registers.
@@ -469,13 +681,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // this workgroup's partial state per head: (acc[d], M, L)
-    float *mypart = a.part + (size_t)blockIdx.x * HC * kPartStride<D>;  // split index = workgroup
-    for (int v = tid; v < HC * D / 4; v += NW * 64) {
+    // one (head hh, four consecutive d) item of this workgroup's partial
+    // state: acc[d..d+3], the slots' maximum M and L = sum 2^(m - M) l
+    auto slot_merge = [&](int v, float4 &x, float &M, float &lsum, bool want_l) {
         const int hh = v / (D / 4);
         const int d = 4 * (v % (D / 4));
         float ws[NSLOT];
-        float M = kNegInf;
+        M = kNegInf;
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl) {
             ws[sl] = s_m[hh][sl];
@@ -483,7 +695,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl) ws[sl] = fast_exp2(ws[sl] - M);  // m, M >= kMinRef: no NaN
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        x = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl) {
             const float4 y = ld4(&s_acc[sl][hh][d]);
@@ -492,11 +704,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
             x.z += ws[sl] * y.z;
             x.w += ws[sl] * y.w;
         }
-        float lsum = 0.f;
-        if (d == 0 || MERGE == kMergeDirect) {
+        lsum = 0.f;
+        if (want_l) {
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) lsum += ws[sl] * s_l[hh][sl];
         }
+    };
+
+    if constexpr (MERGE == kMergeFused) {
+        decode_fused_merge<D, HC, NW>(a, slot_merge, tid, unit, split, b, bg, h0, hl0, nh);
+        return;
+    }
+
+    // this workgroup's partial state per head: (acc[d], M, L)
+    float *mypart = a.part + (size_t)blockIdx.x * HC * kPartStride<D>;  // split index = workgroup
+    for (int v = tid; v < HC * D / 4; v += NW * 64) {
+        const int hh = v / (D / 4);
+        const int d = 4 * (v % (D / 4));
+        float4 x;
+        float M, lsum;
+        slot_merge(v, x, M, lsum, d == 0 || MERGE == kMergeDirect);
         if constexpr (MERGE == kMergeDirect) {
             // no rows (an idle sequence): 0; an invalid length: NaN
             const bool nan = !sr.valid, zero = !(lsum > 0.f);

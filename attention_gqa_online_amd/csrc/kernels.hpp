@@ -20,7 +20,8 @@ struct DecodePlan {
     uint32_t rows_per_split;  // multiple of the rows one workgroup step covers
     uint32_t w0;              // first attended row
     size_t part_floats;       // partial-state floats in the workspace
-    size_t workspace_bytes;   // partial states (the whole workspace)
+    size_t part_offset;       // bytes before them: the units' arrival counters
+    size_t workspace_bytes;   // counters + partial states (the whole workspace)
 };
 
 // With `append`, the split pass covers [w0, total_seq - 1) and the last row

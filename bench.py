@@ -6,7 +6,8 @@
 One step = one decode step of the batched-decode workload (32 sequences,
 12 Q / 2 KV heads, head_dim 128, 4096 cached tokens): append the new token's
 K/V rows at position 4095 and attend over all 4096 positions, as one
-attn_decode_append call (split pass + merge/append pass). The timed region
+attn_decode_append call (one launch: the split pass, whose last workgroup
+per unit merges the splits and appends). The timed region
 holds exactly --steps such steps back to back, bracketed by
 torch.cuda.synchronize(); inputs rotate over three independent cache sets
 (3 x 256 MiB, larger than the 256 MB Infinity Cache) so every step reads its
@@ -14,9 +15,8 @@ K/V from HBM. value = algorithmic K+V bytes per step / step time.
 
 roofline: the attn_decode_append call, timed with HIP events recorded around
 each call on the stream it is launched on; achieved = algorithmic K+V bytes
-(each attended K and V row read once) / mean event time. The call is two
-kernels (the split pass and the merge pass); their rocprofv3 durations add up
-to the event time less the gap between them.
+(each attended K and V row read once) / mean event time. The call is one
+kernel, whose rocprofv3 duration matches the event time.
 
 cpu_baseline: the fp64 oracle on this host's cores over the same decode
 workload (all 32 x 12 heads, repeated to >= 10 s).
@@ -155,8 +155,8 @@ def bench_headline(args, dev):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("attn_decode_append"),
-            "kernel": "attn_decode_append: decode_kernel<128, 6, ...> split pass + "
-                      "decode_merge_kernel<128, 6> merge/append pass",
+            "kernel": "attn_decode_append: decode_kernel<128, 6, ...> split pass with "
+                      "the merge and append in its last workgroup per unit",
             "kernel_mean_us": round(mean_kern * 1e3, 2),
             "per_call_median_us": round(statistics.median(kern_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": bytes_}

@@ -94,9 +94,16 @@ attn_status attn_prefill_causal(const float *q, const float *k, const float *v,
  * Size in bytes of the decode workspace for these shapes (glia honeycrisp
  * "attention.rs" page: the decode module doc and its Params struct). Pure
  * host function; 0 if the shapes are invalid. Any device buffer at least this
- * large serves; its contents on entry do not matter (no clearing needed) and
- * are scratch afterwards. Calls that run concurrently need separate
- * workspaces; calls ordered on one stream may share one.
+ * large serves, provided it was zero-filled before its first use (hipMemset,
+ * a fill kernel, torch.zeros): it begins with a block of 32-bit arrival
+ * counters, one per work unit, which every call leaves at zero again: the
+ * first 65536 bytes, or 4 * batch * num_heads bytes rounded up to a multiple
+ * of 256 where that is more. The rest holds partial states, scratch that
+ * need not be cleared. Calls that run concurrently need separate workspaces.
+ * Calls ordered on one stream may share one whatever their shapes while
+ * batch * num_heads <= 16384 (all of them then have the same counter block);
+ * beyond that, only calls of the same batch, num_heads, kv_heads and
+ * head_dim, unless the workspace is zero-filled again in between.
  */
 size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads,
                                    uint32_t kv_heads, uint32_t head_dim,
@@ -120,11 +127,12 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads,
  * Rows before w0 are never read. The current token is expected to be in the
  * cache already (kv_append at position total_seq - 1 first).
  *
- * workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes
- * (see above). The attended range is split over many workgroups; each writes
- * its partial (max, sum, accumulator) state per head into the workspace, and
- * a second kernel, launched after the first on the same stream, merges the
- * partial states of every (sequence, head) and writes out.
+ * workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
+ * zero-filled before its first use (see above). The attended range is split
+ * over many workgroups of one launch; each writes its partial (max, sum,
+ * accumulator) state per head into the workspace and counts itself in on its
+ * unit's arrival counter, and the last workgroup of each unit merges the
+ * partial states of its heads and writes out.
  *
  * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, kv_heads == 0,
  * num_heads % kv_heads != 0, total_seq == 0, total_seq > max_seq,
@@ -159,8 +167,8 @@ attn_status attn_decode(const float *q, const float *k_cache,
  * not read back from the cache. Sources must not overlap the caches.
  *
  * workspace: at least attn_decode_workspace_bytes(batch, num_heads, kv_heads,
- * head_dim, position + 1, window) bytes, contents irrelevant (may be null
- * when that size is 0).
+ * head_dim, position + 1, window) bytes, zero-filled before its first use
+ * (may be null when that size is 0).
  *
  * Errors: as attn_decode (with total_seq = position + 1), plus position >=
  * max_seq. batch == 0 returns ATTN_OK without a launch; num_heads == 0 only
@@ -277,7 +285,9 @@ attn_status kv_append_rows(const float *k_src, const float *v_src, float *k_cach
  * row read.
  *
  * workspace: at least attn_decode_workspace_bytes(batch, num_heads,
- * kv_heads, head_dim, seq_bound, window) bytes, contents irrelevant.
+ * kv_heads, head_dim, seq_bound, window) bytes, zero-filled before its
+ * first use as for attn_decode (these calls neither read nor change the
+ * arrival counters: their split pass and merge pass are two launches).
  *
  * Errors: as attn_decode with total_seq replaced by seq_bound, plus a null
  * or misaligned (4-byte) seq_lens. batch == 0 or num_heads == 0 returns

@@ -129,10 +129,14 @@ def test_decode_workspace_sizes(lib):
     assert a > 0 and b > 0
     # a window bounds the work: same size as an unwindowed cache of that length
     assert f(16, 32, 8, 128, 32768, 4096) == f(16, 32, 8, 128, 4096, 0)
-    # generous upper bound: one partial state per 32 attended rows and head
-    for args in [(32, 12, 2, 128, 4096, 0), (1, 64, 1, 64, 100000, 0), (3, 7, 7, 32, 1, 0)]:
+    # the counter block (65536 bytes up to 16384 units, 4 bytes per unit past
+    # that), then a generous upper bound on the partial states: one per 32
+    # attended rows and head
+    for args in [(32, 12, 2, 128, 4096, 0), (1, 64, 1, 64, 100000, 0), (3, 7, 7, 32, 1, 0),
+                 (2048, 16, 2, 128, 64, 0)]:
         bsz, hq, hkv, d, t, w = args
-        assert f(*args) <= 256 + 4 * bsz * hkv * 2 + 4 * bsz * hq * (d + 2) * (t // 32 + 2) * 2
+        cnt = max(65536, (4 * bsz * hq + 255) // 256 * 256)
+        assert 65536 < f(*args) <= cnt + 4 * bsz * hq * (d + 4) * (t // 32 + 2) * 2
 
 
 def test_kv_append_argument_rules(lib):

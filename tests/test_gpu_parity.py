@@ -45,6 +45,16 @@ def _assert_close(got, ref, vmax, what):
     return err
 
 
+def _poisoned_ws(nbytes, batch, num_heads, dev):
+    """A decode workspace of every byte 0xFF (NaN floats: a partial state read
+    before this call wrote it shows as NaN), except the arrival counters,
+    which must be zero before the first use: the first 65536 bytes, or
+    4 * batch * num_heads rounded up to 256 where that is more."""
+    ws = torch.full((max(1, nbytes),), 0xFF, dtype=torch.uint8, device=dev)
+    ws[: max(65536, (4 * batch * num_heads + 255) // 256 * 256)] = 0
+    return ws
+
+
 # ------------------------------------------------------------------ decode
 
 def _gpu_decode(dev, w, q, k, v, ws=None, out=None):
@@ -161,10 +171,11 @@ def test_decode_large_scores_stay_finite(dev):
 
 
 def test_decode_deterministic_and_workspace_reused(dev):
-    """Two identical calls give identical bits; one workspace, never cleared
-    (filled with NaN bytes up front), serves calls of different shapes."""
+    """Two identical calls give identical bits; one workspace, cleared only
+    where the counters are (the rest NaN bytes up front), serves calls of
+    different shapes."""
     big = A.attn_decode_workspace_bytes(32, 12, 2, 128, 4096, 0)
-    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device=dev)
+    ws = _poisoned_ws(big, 32, 12, dev)
     w, (q, k, v) = _decode_case(8, 12, 2, 128, 3000, 2900, seed=9)
     a = _gpu_decode(dev, w, q, k, v, ws=ws)
     b = _gpu_decode(dev, w, q, k, v, ws=ws)
@@ -174,6 +185,63 @@ def test_decode_deterministic_and_workspace_reused(dev):
                   _vmax_decode(w2, v2), "reused workspace")
     _assert_close(_gpu_decode(dev, w, q, k, v, ws=ws), _ref_decode(w, q, k, v),
                   _vmax_decode(w, v), "reused workspace, first shape again")
+
+
+FUSED_MERGE_CASES = [
+    # (batch, hq, hkv, d, max_seq, position, window)
+    (3, 12, 2, 128, 3000, 2999, 0),    # 6 units: a unit's splits on several XCDs
+    (1, 8, 1, 128, 20000, 19999, 0),   # one unit, many splits (several merge rounds)
+    (5, 12, 2, 224, 2000, 1999, 300),  # two head chunks per KV head, window
+    (7, 16, 8, 256, 900, 700, 0),      # two (head, d) items per thread in the merge
+]
+
+
+@pytest.mark.parametrize("case", FUSED_MERGE_CASES,
+                         ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_pos{}_w{}".format(*c))
+def test_decode_fused_merge_alternating_inputs(dev, case):
+    """The last workgroup of each unit merges the partial states the other
+    workgroups of the same launch wrote. Two input sets alternate over one
+    workspace (NaN bytes apart from its counters), four decode steps and four
+    plain decodes: a state left over from the previous call, or one not yet
+    visible to the merging workgroup, would give a wrong or NaN output, and
+    counters not returned to zero would leave the next call's output unwritten
+    (NaN)."""
+    b, hq, hkv, d, ms, pos, win = case
+    ws = _poisoned_ws(A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win), b, hq, dev)
+    sets = []
+    for i in range(2):
+        seed = 700 + 11 * i + sum(case) % 89
+        w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, pos + 1, window=win, seed=seed)
+        kn, vn = synth.append_inputs(b, hkv, d, seed=seed + 1)
+        kf, vf = k.copy(), v.copy()
+        oracle.kv_append(kn, vn, kf, vf, b, hkv, d, ms, pos)
+        sets.append((w, q, k, v, kn, vn, kf, vf, _ref_decode(w, q, kf, vf), _vmax_decode(w, vf)))
+    for call in range(4):
+        w, q, k, v, kn, vn, kf, vf, ref, vmax = sets[call % 2]
+        kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+        out = torch.full((b, hq, d), float("nan"), device=dev)
+        A.attn_decode_append(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
+                             torch.from_numpy(vn).to(dev), kd, vd, out, b, hq, hkv, d, ms, pos,
+                             win, w.scale, ws)
+        got_plain = _gpu_decode(dev, w, q, kf, vf, ws=ws)
+        torch.cuda.synchronize()
+        _assert_close(out.cpu().numpy(), ref, vmax, f"decode step, call {call}")
+        _assert_close(got_plain, ref, vmax, f"decode, call {call}")
+        assert np.array_equal(kd.cpu().numpy(), kf) and np.array_equal(vd.cpu().numpy(), vf)
+
+
+def test_decode_workspace_shared_by_unit_counts(dev):
+    """One workspace (zeroed once) serves calls whose unit counts differ: a
+    4-unit call writes its partial states, then a 64-unit call must still find
+    its counters at zero, then the 4-unit call again."""
+    ws = torch.zeros(max(A.attn_decode_workspace_bytes(32, 12, 2, 128, 2048, 0),
+                         A.attn_decode_workspace_bytes(2, 12, 2, 128, 6000, 0)),
+                     dtype=torch.uint8, device=dev)
+    small = _decode_case(2, 12, 2, 128, 6000, 6000, seed=31)
+    large = _decode_case(32, 12, 2, 128, 2048, 2048, seed=32)
+    for w, (q, k, v) in (small, large, small, large):
+        _assert_close(_gpu_decode(dev, w, q, k, v, ws=ws), _ref_decode(w, q, k, v),
+                      _vmax_decode(w, v), f"shared workspace, batch {w.batch}")
 
 
 def test_decode_on_a_side_stream(dev):
@@ -216,8 +284,7 @@ def _decode_append_case(dev, case, seed):
     kn, vn = synth.append_inputs(b, hkv, d, seed=seed + 1)
     kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
     out = torch.full((b, hq, d), float("nan"), device=dev)
-    ws = torch.full((max(1, A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win)),),
-                    0xFF, dtype=torch.uint8, device=dev)
+    ws = _poisoned_ws(A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win), b, hq, dev)
     A.attn_decode_append(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
                          torch.from_numpy(vn).to(dev), kd, vd, out, b, hq, hkv, d, ms, pos,
                          win, w.scale, ws)
@@ -278,8 +345,7 @@ def _decode_rope_case(dev, case, seed, scale_angles=1.0):
     cos_t, sin_t = synth.rope_tables(d, pos * scale_angles)
     kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
     out = torch.full((b, hq, d), float("nan"), device=dev)
-    ws = torch.full((max(1, A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win)),),
-                    0xFF, dtype=torch.uint8, device=dev)
+    ws = _poisoned_ws(A.attn_decode_workspace_bytes(b, hq, hkv, d, pos + 1, win), b, hq, dev)
     A.attn_decode_rope_append(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
                               torch.from_numpy(vn).to(dev), torch.from_numpy(cos_t).to(dev),
                               torch.from_numpy(sin_t).to(dev), kd, vd, out, b, hq, hkv, d, ms,
@@ -535,8 +601,7 @@ def test_decode_varlen_matches_oracle(dev, case):
     w, q, k, v, lens = _varlen_inputs(case, seed=sum(case) % 883)
     b, hq, hkv, d, ms, bound, win, _ = case
     out = torch.full((b, hq, d), float("nan"), device=dev)
-    ws = torch.full((A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win),), 0xFF,
-                    dtype=torch.uint8, device=dev)
+    ws = _poisoned_ws(A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win), b, hq, dev)
     A.attn_decode_varlen(torch.from_numpy(q).to(dev), torch.from_numpy(k).to(dev),
                          torch.from_numpy(v).to(dev), out,
                          torch.from_numpy(lens.astype(np.int32)).to(dev), b, hq, hkv, d, ms,
@@ -594,7 +659,7 @@ def test_decode_append_varlen_matches_oracle(dev, case):
     kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
     out = torch.full((b, hq, d), float("nan"), device=dev)
     nws = A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win)
-    ws = torch.full((max(1, nws),), 0xFF, dtype=torch.uint8, device=dev)
+    ws = _poisoned_ws(nws, b, hq, dev)
     A.attn_decode_append_varlen(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
                                 torch.from_numpy(vn).to(dev), kd, vd, out,
                                 torch.from_numpy(pos.astype(np.int32)).to(dev), b, hq, hkv, d,
@@ -1091,8 +1156,7 @@ def test_decode_rope_append_varlen_matches_oracle(dev, case):
     sin_t = np.ascontiguousarray(np.stack([t[1] for t in tabs]))
     kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
     out = torch.full((b, hq, d), float("nan"), device=dev)
-    ws = torch.full((A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win),), 0xFF,
-                    dtype=torch.uint8, device=dev)
+    ws = _poisoned_ws(A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win), b, hq, dev)
     A.attn_decode_rope_append_varlen(
         torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev),
         torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev), kd, vd, out,
