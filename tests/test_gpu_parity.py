@@ -192,7 +192,7 @@ FUSED_MERGE_CASES = [
     (3, 12, 2, 128, 3000, 2999, 0),    # 6 units: a unit's splits on several XCDs
     (1, 8, 1, 128, 20000, 19999, 0),   # one unit, many splits (several merge rounds)
     (5, 12, 2, 224, 2000, 1999, 300),  # two head chunks per KV head, window
-    (7, 16, 8, 256, 900, 700, 0),      # two (head, d) items per thread in the merge
+    (3, 16, 2, 256, 900, 700, 0),      # 8 heads x 64 float4 items: two per thread in the merge
 ]
 
 
