@@ -44,16 +44,14 @@ constexpr int max_head_chunk(int d) {
     return hc < 8 ? hc : 8;
 }
 
-// Threads of a merge workgroup: one per d, rounded up to whole waves.
-constexpr int merge_threads(int d) { return d <= 64 ? d : (d + 63) / 64 * 64; }
-
-// Uniform lengths: one launch. With a single split per unit and no appended
-// row it writes the normalised output itself; otherwise the last workgroup
-// of each unit merges the splits' partial states (kMergeFused). With no row
-// before the appended one (n_split 0) only the merge kernel runs.
-// Per-sequence lengths: pass 1 writes one partial state per (unit, split,
-// head); pass 2, ordered after it on the same stream, merges the splits of
-// every (unit, head).
+// One launch per call. With a single split per unit and no appended row
+// each workgroup writes its unit's normalised output itself; otherwise the
+// last workgroup of each unit to finish merges the units' partial states
+// and the appended row (kMergeFused). With no row before the appended one
+// (n_split 0) every unit gets one workgroup over an empty range, which only
+// folds in the new row. With per-sequence lengths the grid holds the
+// proportional splits and one more workgroup per unit, so the units with no
+// rows in the split pass (idle, only the new row, invalid) get one each.
 template <int D, int HC>
 hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStream_t stream) {
     constexpr int LPR = lanes_per_row(D);
@@ -67,24 +65,21 @@ hipError_t launch_hc(DecodeArgs args, uint32_t units, uint32_t n_split, hipStrea
                                dim3(units), dim3(kDecodeWaves * 64), 0, stream, args);
         return hipGetLastError();
     }
-    if (args.lens == nullptr && n_split > 0) {
+    if (args.lens == nullptr) {
+        if (n_split == 0) {  // only the appended row
+            args.n_split = 1;
+            args.rows_per_split = 0;
+            n_split = 1;
+        }
         hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeFused, false>),
                            dim3(units * n_split), dim3(kDecodeWaves * 64), 0, stream, args);
         return hipGetLastError();
     }
-    if (n_split > 0) {
-        // proportional splits: at most g_target + units of them hold rows;
-        // the workgroups past the last one exit at once
-        args.g_target = kTargetWorkgroupsVarlen(units);
-        args.min_rows = kDecodeWaves * kMinRowsPerWave;
-        args.rows_step = kDecodeWaves * (64 / LPR);
-        hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergePartialOnly, true>),
-                           dim3(args.g_target + units), dim3(kDecodeWaves * 64), 0, stream, args);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((decode_merge_kernel<D, HC>), dim3(units * HC), dim3(merge_threads(D)), 0,
-                       stream, args);
+    args.g_target = kTargetWorkgroupsVarlen(units);
+    args.min_rows = kDecodeWaves * kMinRowsPerWave;
+    args.rows_step = kDecodeWaves * (64 / LPR);
+    hipLaunchKernelGGL((decode_kernel<D, HC, LPR, kDecodeWaves, kPrefetch, kMergeFused, true>),
+                       dim3(args.g_target + units), dim3(kDecodeWaves * 64), 0, stream, args);
     return hipGetLastError();
 }
 
@@ -159,8 +154,8 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     p.rows_per_split = rows;
     p.n_split = ceil_div(len, rows);
     // per-sequence lengths: the proportional table has at most
-    // target + units splits (the split pass runs unless the plan has a
-    // single split and no appended row)
+    // target + units splits (used unless the plan has a single split and no
+    // appended row)
     const size_t slots = varlen && !(p.n_split == 1 && !append)
                              ? (size_t)kTargetWorkgroupsVarlen(p.units) + p.units
                              : (size_t)p.units * p.n_split;

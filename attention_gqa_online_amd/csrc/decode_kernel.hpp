@@ -31,9 +31,8 @@
 // state (m, l, acc[d]) per head, written to the workspace; the last
 // workgroup of each unit to finish (an arrival counter per unit) folds the
 // partial states of its heads with a running log-sum-exp and writes the
-// normalised output (decode_fused_merge). With per-sequence lengths a second
-// kernel on the same stream does that fold instead (decode_merge_kernel).
-// When the call also appends the current token (attn_decode_append), the
+// normalised output (decode_fused_merge), all in one launch. When the call
+// also appends the current token (attn_decode_append), the
 // split pass covers the rows before it and the merge folds the new row in as
 // one more partial state, scored from the new K row itself, and writes the
 // new K and V rows into the caches (rotated first when the call applies
@@ -55,7 +54,7 @@ struct DecodeArgs {
     uint32_t *cnt;    // [units] arrival counters of the fused merge: zero between calls
     float *part;      // [splits][HC][D + 4]: acc[D], m, l, 2 pad; split s of unit u at s * units + u
                       // (per-sequence lengths: proportional splits numbered unit by unit)
-    // fused append (merge kernel only): new rows [B, Hkv, D], or null
+    // fused append (the merging workgroups): new rows [B, Hkv, D], or null
     const float *k_new;
     const float *v_new;
     float *k_dst;     // the caches, written at row `position`
@@ -158,57 +157,75 @@ __device__ __forceinline__ uint64_t prop_total(const DecodeArgs &a, int lane) {
 struct PropHit {
     uint32_t unit, first, n, rows;
     bool found;
-    uint32_t len;  // prop_locate: the unit's per-sequence length value
+    uint32_t len;  // the unit's per-sequence length value
 };
 
-// The unit holding split index w (by_unit = false), or unit w itself
-// (by_unit = true); first = its first split index, n its split count.
+// Workgroup w of the split pass: the unit holding split index w, first = its
+// first split index, n its split count. The workgroups past the last split
+// (S splits in all) take the units with no rows in the split pass, in unit
+// order: workgroup S + k the k-th such unit (n = 0), which then has only its
+// appended row, or is idle, or has an invalid length. With at most W units
+// (the usual case) each lane loads its unit's length once and the table is
+// one scan: a single dependent global load before the split pass can issue
+// its first K/V loads.
 template <int W>
-__device__ __forceinline__ PropHit prop_find(const DecodeArgs &a, uint64_t T, uint32_t w,
-                                             bool by_unit, int lane) {
-    uint32_t carry = 0;
-    for (uint32_t base = 0; base < a.units; base += W) {
-        const uint32_t u = base + lane;
-        const PropSplit ps = u < a.units ? prop_split(a, unit_rows(a, u), T) : PropSplit{0, 0};
-        const uint32_t incl = wave_incl_scan<W>(ps.n, lane);
-        const uint32_t S = carry + incl - ps.n;
-        const bool hit = by_unit ? u == w : (ps.n != 0 && S <= w && w - S < ps.n);
-        const unsigned long long mask = __ballot(hit);
-        if (mask != 0) {
-            const int src = __ffsll((long long)mask) - 1;
-            return {(uint32_t)__shfl((int)u, src), (uint32_t)__shfl((int)S, src),
-                    (uint32_t)__shfl((int)ps.n, src), (uint32_t)__shfl((int)ps.rows, src), true,
-                    0};
-        }
-        carry += (uint32_t)__shfl((int)incl, W - 1);
-    }
-    return {0, 0, 0, 0, false, 0};
-}
-
-// prop_find with the batch total, and the found unit's length value. With
-// at most W units (the usual case) each lane loads its unit's length once and
-// the table is one scan: a single dependent global load before the split
-// pass can issue its first K/V loads.
-template <int W>
-__device__ __forceinline__ PropHit prop_locate(const DecodeArgs &a, uint32_t w, bool by_unit,
-                                               int lane) {
+__device__ __forceinline__ PropHit prop_locate(const DecodeArgs &a, uint32_t w, int lane) {
     if (a.units > W) {
-        PropHit ph = prop_find<W>(a, prop_total<W>(a, lane), w, by_unit, lane);
-        if (ph.found) ph.len = a.lens[(ph.unit / a.n_chunks) / a.kv_heads];
-        return ph;
+        const uint64_t T = prop_total<W>(a, lane);
+        uint32_t carry = 0;  // splits before this chunk
+        for (uint32_t base = 0; base < a.units; base += W) {
+            const uint32_t u = base + lane;
+            const PropSplit ps = u < a.units ? prop_split(a, unit_rows(a, u), T) : PropSplit{0, 0};
+            const uint32_t incl = wave_incl_scan<W>(ps.n, lane);
+            const uint32_t S = carry + incl - ps.n;
+            const unsigned long long mask = __ballot(ps.n != 0 && S <= w && w - S < ps.n);
+            if (mask != 0) {
+                const int src = __ffsll((long long)mask) - 1;
+                const uint32_t un = (uint32_t)__shfl((int)u, src);
+                return {un, (uint32_t)__shfl((int)S, src), (uint32_t)__shfl((int)ps.n, src),
+                        (uint32_t)__shfl((int)ps.rows, src), true,
+                        a.lens[(un / a.n_chunks) / a.kv_heads]};
+            }
+            carry += (uint32_t)__shfl((int)incl, W - 1);
+        }
+        uint32_t k = w - carry;  // past the last split: the k-th unit with no rows
+        for (uint32_t base = 0; base < a.units; base += W) {
+            const uint32_t u = base + lane;
+            const bool z = u < a.units && unit_rows(a, u) == 0;
+            const unsigned long long zm = __ballot(z);
+            const uint32_t cnt = (uint32_t)__popcll(zm);
+            if (k < cnt) {
+                const uint32_t rank = (uint32_t)__popcll(zm & ((1ull << lane) - 1ull));
+                const unsigned long long hm = __ballot(z && rank == k);
+                const uint32_t un = base + (uint32_t)(__ffsll((long long)hm) - 1);
+                return {un, 0, 0, 0, true, a.lens[(un / a.n_chunks) / a.kv_heads]};
+            }
+            k -= cnt;
+        }
+        return {0, 0, 0, 0, false, 0};
     }
     const uint32_t u = lane;
     const bool in = u < a.units;
     const uint32_t len = in ? a.lens[(u / a.n_chunks) / a.kv_heads] : 0;
     const SeqRange r = seq_range_len(a, len);
     const uint32_t L = in && r.hi > r.w0 ? r.hi - r.w0 : 0;
-    const uint64_t T = wave_sum_u64<W>(L);
-    const PropSplit ps = in ? prop_split(a, L, T) : PropSplit{0, 0};
+    const uint64_t T1 = wave_sum_u64<W>(L);
+    const PropSplit ps = in ? prop_split(a, L, T1) : PropSplit{0, 0};
     const uint32_t incl = wave_incl_scan<W>(ps.n, lane);
     const uint32_t S = incl - ps.n;
-    const bool hit = in && (by_unit ? u == w : (ps.n != 0 && S <= w && w - S < ps.n));
-    const unsigned long long mask = __ballot(hit);
-    if (mask == 0) return {0, 0, 0, 0, false, 0};
+    unsigned long long mask = __ballot(in && ps.n != 0 && S <= w && w - S < ps.n);
+    if (mask == 0) {
+        // past the last split: the k-th unit with no rows
+        const uint32_t total = (uint32_t)__shfl((int)incl, W - 1);
+        const uint32_t k = w - total;
+        const bool z = in && ps.n == 0;
+        const unsigned long long zm = __ballot(z);
+        const uint32_t rank = (uint32_t)__popcll(zm & ((1ull << lane) - 1ull));
+        mask = __ballot(z && rank == k);
+        if (mask == 0) return {0, 0, 0, 0, false, 0};
+        const int src = __ffsll((long long)mask) - 1;
+        return {(uint32_t)src, 0, 0, 0, true, (uint32_t)__shfl((int)len, src)};
+    }
     const int src = __ffsll((long long)mask) - 1;
     return {(uint32_t)__shfl((int)u, src), (uint32_t)__shfl((int)S, src),
             (uint32_t)__shfl((int)ps.n, src), (uint32_t)__shfl((int)ps.rows, src), true,
@@ -220,11 +237,11 @@ __device__ __forceinline__ PropHit prop_locate(const DecodeArgs &a, uint32_t w, 
 template <int D>
 constexpr int kPartStride = D + 4;
 
-// What the split pass writes: one partial state per (unit, split, head) for
-// the merge kernel, or, with a single split per unit, the normalised output.
-// kMergeFused: the split pass also merges: the last workgroup of a unit to
-// finish folds every split's state (and the appended row) and writes out.
-enum DecodeMerge { kMergePartialOnly = 1, kMergeFused = 2, kMergeDirect = 3 };
+// kMergeFused: every workgroup writes one partial state per head, and the
+// last workgroup of a unit to finish folds every split's state (and the
+// appended row) and writes out. kMergeDirect: a single split per unit and no
+// appended row, so each workgroup writes its unit's normalised output.
+enum DecodeMerge { kMergeFused = 2, kMergeDirect = 3 };
 
 // Partial states that another workgroup of the same launch reads back go
 // through agent-scope (relaxed) atomic stores and loads, 8 bytes each: these
@@ -257,9 +274,19 @@ __device__ __forceinline__ float2 ld_dev2(const float *p) {
 // score is summed over the items of a head in LDS), then every split's state
 // in index order, and writes acc / l. It also writes the new K and V rows
 // into the caches (chunk 0 of each KV head).
+// Where a unit's partial states live: ns splits, split s at slot
+// slot0 + s * sstride, this workgroup's at `mine`; `pos` is the sequence's
+// appended row and valid = false marks an invalid per-sequence length.
+struct MergeSlots {
+    uint32_t ns;
+    size_t slot0, sstride, mine;
+    uint32_t pos;
+    bool valid;
+};
+
 template <int D, int HC, int NW, typename SlotMerge>
 __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerge &slot_merge,
-                                                   int tid, uint32_t unit, uint32_t split,
+                                                   int tid, uint32_t unit, const MergeSlots &ms,
                                                    uint32_t b, uint32_t bg, uint32_t h0,
                                                    uint32_t hl0, int nh) {
     constexpr int NT = NW * 64;
@@ -285,9 +312,19 @@ __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerg
         slot_merge(v, num[it], M[it], den[it], true);
     }
 
-    const uint32_t ns = a.n_split;
+    if (!ms.valid) {  // an invalid length: NaN output, nothing appended
+#pragma unroll
+        for (int it = 0; it < NITEM; ++it) {
+            if (!own[it] || hv[it] >= nh) continue;
+            const float nan = __builtin_nanf("");
+            st4(a.out + ((size_t)b * a.num_heads + h0 + hv[it]) * D + dv[it],
+                make_float4(nan, nan, nan, nan));
+        }
+        return;
+    }
+    const uint32_t ns = ms.ns;
     if (ns > 1) {
-        float *mypart = a.part + (size_t)blockIdx.x * HC * PS;  // split index = workgroup
+        float *mypart = a.part + ms.mine * HC * PS;
 #pragma unroll
         for (int it = 0; it < NITEM; ++it) {
             if (!own[it]) continue;
@@ -336,8 +373,7 @@ __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerg
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t sp = min(s0 + i, ns - 1);
-                const float *ps =
-                    a.part + ((size_t)sp * a.units + unit) * HC * PS + hv[it] * PS;
+                const float *ps = a.part + (ms.slot0 + sp * ms.sstride) * HC * PS + hv[it] * PS;
                 ml[it][i] = ld_dev2(ps + D);
                 const float2 lo = ld_dev2(ps + dv[it]);
                 const float2 hi = ld_dev2(ps + dv[it] + 2);
@@ -403,7 +439,7 @@ __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerg
             num[it] = vn[it];
             den[it] = 1.f;
             if (hl0 == 0 && hv[it] == 0 && own[it]) {  // one writer per (sequence, KV head)
-                const size_t dst = ((size_t)bg * a.max_seq + a.position) * D + dv[it];
+                const size_t dst = ((size_t)bg * a.max_seq + ms.pos) * D + dv[it];
                 st4(a.k_dst + dst, kn[it]);
                 st4(a.v_dst + dst, vn[it]);
             }
@@ -427,8 +463,11 @@ __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerg
 #pragma unroll
     for (int it = 0; it < NITEM; ++it) {
         if (!own[it] || hv[it] >= nh) continue;
-        const float4 o = make_float4(num[it].x / den[it], num[it].y / den[it],
-                                     num[it].z / den[it], num[it].w / den[it]);
+        // den is 0 only for an idle sequence (no rows, nothing appended): 0
+        const bool zero = !(den[it] > 0.f);
+        const float4 o = zero ? make_float4(0.f, 0.f, 0.f, 0.f)
+                              : make_float4(num[it].x / den[it], num[it].y / den[it],
+                                            num[it].z / den[it], num[it].w / den[it]);
         st4(a.out + ((size_t)b * a.num_heads + h0 + hv[it]) * D + dv[it], o);
     }
 }
@@ -456,23 +495,26 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 
     // split-major numbering: the splits of a unit are units apart, so with
     // units a multiple of 8 they land on one XCD (workgroups go round-robin
-    // over the 8 XCDs), and so does the unit's merge workgroup
+    // over the 8 XCDs)
     uint32_t split = blockIdx.x / a.units;
     uint32_t unit = blockIdx.x % a.units;
     uint32_t rps = a.rows_per_split;
     bool have_len = false;  // the unit's length value is already in `len`
     uint32_t len = 0;
-    if constexpr (MERGE == kMergePartialOnly && VARLEN) {
+    MergeSlots msl{a.n_split, unit, a.units, blockIdx.x, a.position, true};
+    if constexpr (MERGE == kMergeFused && VARLEN) {
         {
             // per-sequence lengths: workgroup w is split w - first(u) of the
-            // unit u whose splits include w (proportional table)
-            const PropHit ph = prop_locate<64>(a, blockIdx.x, false, lane);
-            if (!ph.found) return;  // past the last split (uniform)
+            // unit u whose splits include w (proportional table), or takes a
+            // unit with no rows (an empty range, then only the merge)
+            const PropHit ph = prop_locate<64>(a, blockIdx.x, lane);
+            if (!ph.found) return;  // past the last unit (uniform)
             unit = ph.unit;
-            split = blockIdx.x - ph.first;
+            split = ph.n != 0 ? blockIdx.x - ph.first : 0;
             rps = ph.rows;
             len = ph.len;
             have_len = true;
+            msl = MergeSlots{ph.n != 0 ? ph.n : 1u, ph.first, 1, blockIdx.x, 0, true};
         }
     }
     const uint32_t chunk = unit % a.n_chunks;
@@ -488,6 +530,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     const SeqRange sr = !VARLEN ? SeqRange{a.w0, a.total_seq, a.position, true}
                         : have_len ? seq_range_len(a, len)
                                    : seq_range(a, b);
+    msl.pos = sr.pos;
+    msl.valid = sr.valid;
     const uint32_t ws0 = sr.w0 + split * rps;
     const uint32_t ws1 = min(ws0 + rps, sr.hi);
     const uint32_t ra = ws0 + wave * RPT;
@@ -712,163 +756,29 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     };
 
     if constexpr (MERGE == kMergeFused) {
-        decode_fused_merge<D, HC, NW>(a, slot_merge, tid, unit, split, b, bg, h0, hl0, nh);
+        decode_fused_merge<D, HC, NW>(a, slot_merge, tid, unit, msl, b, bg, h0, hl0, nh);
         return;
     }
 
-    // this workgroup's partial state per head: (acc[d], M, L)
-    float *mypart = a.part + (size_t)blockIdx.x * HC * kPartStride<D>;  // split index = workgroup
+    // a single split and no appended row: the normalised output directly
     for (int v = tid; v < HC * D / 4; v += NW * 64) {
         const int hh = v / (D / 4);
         const int d = 4 * (v % (D / 4));
         float4 x;
         float M, lsum;
-        slot_merge(v, x, M, lsum, d == 0 || MERGE == kMergeDirect);
-        if constexpr (MERGE == kMergeDirect) {
-            // no rows (an idle sequence): 0; an invalid length: NaN
-            const bool nan = !sr.valid, zero = !(lsum > 0.f);
-            float4 o;
-            o.x = nan ? __builtin_nanf("") : zero ? 0.f : x.x / lsum;
-            o.y = nan ? __builtin_nanf("") : zero ? 0.f : x.y / lsum;
-            o.z = nan ? __builtin_nanf("") : zero ? 0.f : x.z / lsum;
-            o.w = nan ? __builtin_nanf("") : zero ? 0.f : x.w / lsum;
-            if (hh < nh) st4(a.out + ((size_t)b * a.num_heads + h0 + hh) * D + d, o);
-        } else {
-            float *ph = mypart + hh * kPartStride<D>;
-            st4(ph + d, x);
-            if (d == 0) {
-                ph[D] = M;
-                ph[D + 1] = lsum;
-            }
-        }
+        slot_merge(v, x, M, lsum, true);
+        // no rows (an idle sequence): 0; an invalid length: NaN
+        const bool nan = !sr.valid, zero = !(lsum > 0.f);
+        float4 o;
+        o.x = nan ? __builtin_nanf("") : zero ? 0.f : x.x / lsum;
+        o.y = nan ? __builtin_nanf("") : zero ? 0.f : x.y / lsum;
+        o.z = nan ? __builtin_nanf("") : zero ? 0.f : x.z / lsum;
+        o.w = nan ? __builtin_nanf("") : zero ? 0.f : x.w / lsum;
+        if (hh < nh) st4(a.out + ((size_t)b * a.num_heads + h0 + hh) * D + d, o);
     }
 }
 
-// Sum over the NT threads of a workgroup (NT = 32, or a multiple of 64).
-template <int NT>
-__device__ __forceinline__ float block_sum(float x) {
-    constexpr int W = NT < 64 ? NT : 64;
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, W);
-    if constexpr (NT <= 64) {
-        return x;
-    } else {
-        __shared__ float red[NT / 64];
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-        __syncthreads();
-        float t = 0.f;
-#pragma unroll
-        for (int i = 0; i < NT / 64; ++i) t += red[i];
-        return t;
-    }
-}
-
-// Second pass of the two-kernel decode: one workgroup of D threads per
-// (unit, head); thread d folds the n_split partial states (acc[d], m, l) into
-// a running log-sum-exp (M, num, den), eight splits per round so the loads of
-// a round are independent, and writes out = num / den. With a fused append
-// the new row enters first as the state (m = its score, l = 1, acc = v_new).
+// Largest number of splits per unit the plan makes.
 constexpr int kMaxSplit = 1024;
-
-template <int D, int HC>
-__global__ __launch_bounds__(D <= 64 ? D : (D + 63) / 64 * 64) void decode_merge_kernel(
-    DecodeArgs a) {
-    // one thread per d, rounded up to whole waves; threads past D re-read
-    // element D - 1, store nothing and add 0 to the new row's score
-    constexpr int NT = D <= 64 ? D : (D + 63) / 64 * 64;
-    const bool live = (int)threadIdx.x < D;
-    const int tid = live ? (int)threadIdx.x : D - 1;
-    const uint32_t unit = blockIdx.x % a.units;
-    const int hh = blockIdx.x / a.units;
-    const uint32_t chunk = unit % a.n_chunks;
-    const uint32_t bg = unit / a.n_chunks;
-    const uint32_t g = bg % a.kv_heads;
-    const uint32_t b = bg / a.kv_heads;
-    const uint32_t hl0 = chunk * HC;
-    if ((int)(a.hpk - hl0) <= hh) return;  // head past this chunk's end
-    const uint32_t h = g * a.hpk + hl0 + hh;
-    uint32_t ns = a.n_split;
-    size_t first = unit;  // the unit's first split index
-    size_t sstride = (size_t)a.units;  // split indices between its splits
-    SeqRange sr;
-    if (a.lens != nullptr && ns != 0) {  // the split pass ran with the proportional table
-        constexpr int W = NT < 64 ? NT : 64;
-        const PropHit ph = prop_locate<W>(a, unit, true, (int)(threadIdx.x & 63));
-        first = ph.first;
-        sstride = 1;
-        ns = ph.n;
-        sr = seq_range_len(a, ph.len);
-    } else {
-        sr = seq_range(a, b);
-    }
-    if (!sr.valid) {  // invalid length: NaN output, nothing appended
-        if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = __builtin_nanf("");
-        return;
-    }
-    constexpr uint32_t SS = HC * kPartStride<D>;  // floats between splits
-    const float *up = a.part + first * SS + hh * kPartStride<D>;
-
-    // partial states are read eight splits per round (independent loads);
-    // a round's entries past ns re-read the last split with weight 0
-    float ms[8], ls[8], xs[8];
-    auto load_round = [&](uint32_t s0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t sp = min(s0 + i, ns - 1);
-            const float *ps = up + (size_t)sp * sstride * SS;
-            ms[i] = s0 + i < ns ? ps[D] : kNegInf;
-            ls[i] = ps[D + 1];
-            xs[i] = ps[tid];
-        }
-    };
-    float M = kNegInf, num = 0.f, den = 0.f;
-    auto fold_round = [&]() {
-        float Mn = M;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) Mn = fmaxf(Mn, ms[i]);
-        const float c = M == kNegInf ? 0.f : fast_exp2(M - Mn);
-        num *= c;
-        den *= c;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float w = ms[i] == kNegInf ? 0.f : fast_exp2(ms[i] - Mn);
-            num += xs[i] * w;
-            den += ls[i] * w;
-        }
-        M = Mn;
-    };
-    if (ns > 0) load_round(0);  // in flight while the new row is scored
-    if (a.k_new != nullptr) {
-        const float *knp = a.k_new + (size_t)bg * D;
-        const float *qp = a.q + ((size_t)b * a.num_heads + h) * D;
-        float kn = knp[tid];
-        float qd = qp[tid];
-        const float vn = a.v_new[(size_t)bg * D + tid];
-        if (a.cos_t != nullptr) {  // rotate the new K row and q (rotate-half)
-            const bool lo = tid < D / 2;
-            const int partner = lo ? tid + D / 2 : tid - D / 2;
-            const size_t ci = (size_t)b * a.cs_stride + tid % (D / 2);
-            const float cc = a.cos_t[ci], ss = a.sin_t[ci];
-            kn = rope_half1(kn, knp[partner], cc, ss, lo);
-            qd = rope_half1(qd, qp[partner], cc, ss, lo);
-        }
-        qd *= a.qscale;
-        M = block_sum<NT>(live ? qd * kn : 0.f);  // the new row's score, log2 units
-        num = vn;
-        den = 1.f;
-        if (hl0 + hh == 0 && live) {  // one writer per (sequence, KV head)
-            const size_t dst = ((size_t)bg * a.max_seq + sr.pos) * D + tid;
-            a.k_dst[dst] = kn;
-            a.v_dst[dst] = vn;
-        }
-    }
-    if (ns > 0) fold_round();
-    for (uint32_t s0 = 8; s0 < ns; s0 += 8) {
-        load_round(s0);
-        fold_round();
-    }
-    // den is 0 only for an idle sequence (no rows, nothing appended)
-    if (live) a.out[((size_t)b * a.num_heads + h) * D + tid] = den > 0.f ? num / den : 0.f;
-}
 
 }  // namespace attn

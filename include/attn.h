@@ -10,7 +10,7 @@
  *                         sliding window
  *   kv_append             write one new K row and V row per (sequence, KV head)
  *                         into the caches
- *   attn_decode_append    kv_append + attn_decode of the same token, two launches
+ *   attn_decode_append    kv_append + attn_decode of the same token in one launch
  *   attn_decode_rope_append
  *                         the same decode step with rotary position embedding
  *                         applied to q and to the new K rows on the way in
@@ -286,8 +286,7 @@ attn_status kv_append_rows(const float *k_src, const float *v_src, float *k_cach
  *
  * workspace: at least attn_decode_workspace_bytes(batch, num_heads,
  * kv_heads, head_dim, seq_bound, window) bytes, zero-filled before its
- * first use as for attn_decode (these calls neither read nor change the
- * arrival counters: their split pass and merge pass are two launches).
+ * first use as for attn_decode.
  *
  * Errors: as attn_decode with total_seq replaced by seq_bound, plus a null
  * or misaligned (4-byte) seq_lens. batch == 0 or num_heads == 0 returns
