@@ -706,6 +706,70 @@ def test_decode_append_varlen_invalid_position_and_no_heads(dev):
                           "valid rows")
 
 
+@pytest.mark.parametrize("rope", [False, True], ids=["plain", "rope"])
+def test_decode_append_varlen_units_without_rows(dev, rope):
+    """More than 64 units (the table is scanned in 64-lane chunks), some with
+    no row before the new one (position 0: the output is the new V row) and
+    one with an invalid position (NaN, no cache write): those units get the
+    grid's spare workgroups, which merge over an empty range."""
+    b, hq, hkv, d, ms, bound, win = 40, 8, 2, 64, 500, 500, 0   # 80 units
+    w = synth.DecodeWorkload("varlen", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=bound, window=win, seed=41)
+    q, k, v = synth.decode_inputs(w)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=42)
+    pos = (synth.seq_lengths(b, bound, seed=43) - 1).astype(np.uint32)
+    pos[[3, 17, 30, 39]] = 0
+    pos[5] = bound                                              # invalid: T_b > seq_bound
+    valid = np.flatnonzero(pos < bound)
+    kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    out = torch.full((b, hq, d), float("nan"), device=dev)
+    ws = _poisoned_ws(A.attn_decode_workspace_bytes(b, hq, hkv, d, bound, win), b, hq, dev)
+    posd = torch.from_numpy(pos.astype(np.int32)).to(dev)
+    kr, vr = k.copy(), v.copy()
+    vmax_pos = np.where(pos < bound, pos.astype(np.int64), -1)    # the invalid one skipped
+    if rope:
+        tabs = [synth.rope_tables(d, int(p) % bound) for p in pos]
+        cos_t = np.ascontiguousarray(np.stack([t[0] for t in tabs]))
+        sin_t = np.ascontiguousarray(np.stack([t[1] for t in tabs]))
+        A.attn_decode_rope_append_varlen(
+            torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev),
+            torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev), kd, vd, out, posd,
+            b, hq, hkv, d, ms, bound, win, w.scale, ws)
+        torch.cuda.synchronize()
+        ref = np.zeros((b, hq, d))
+        for i in valid:   # the oracle's fused step, sequence by sequence (updates kr, vr)
+            ref[i] = oracle.decode_rope_append(q[i:i + 1], kn[i:i + 1], vn[i:i + 1], cos_t[i],
+                                               sin_t[i], kr[i:i + 1], vr[i:i + 1], 1, hq, hkv,
+                                               d, ms, int(pos[i]), win, w.scale)[0]
+        kc, vc = kd.cpu().numpy(), vd.cpu().numpy()
+        assert np.array_equal(vc, vr)
+        for i in range(b):
+            keep = np.arange(ms) != pos[i] if i in valid else np.ones(ms, bool)
+            assert np.array_equal(kc[i][:, keep], k[i][:, keep])
+            if i in valid:
+                err = np.abs(kc[i, :, pos[i]].astype(np.float64) - kr[i, :, pos[i]])
+                assert np.all(err <= _rope_row_bound(kn[i])), (i, float(err.max()))
+        _assert_close(out.cpu().numpy()[valid], ref[valid], _vmax_varlen(w, vr, vmax_pos, plus=1),
+                      "valid sequences")
+    else:
+        A.attn_decode_append_varlen(torch.from_numpy(q).to(dev), torch.from_numpy(kn).to(dev),
+                                    torch.from_numpy(vn).to(dev), kd, vd, out, posd, b, hq, hkv,
+                                    d, ms, bound, win, w.scale, ws)
+        torch.cuda.synchronize()
+        for i in valid:
+            oracle.kv_append(kn[i:i + 1], vn[i:i + 1], kr[i:i + 1], vr[i:i + 1], 1, hkv, d, ms,
+                             int(pos[i]))
+        assert np.array_equal(kd.cpu().numpy(), kr) and np.array_equal(vd.cpu().numpy(), vr)
+        ref = oracle.decode_varlen(q, kr, vr, np.where(pos < bound, pos + 1, 0), b, hq, hkv,
+                                   d, ms, win, w.scale)
+        _assert_close(out.cpu().numpy()[valid], ref[valid], _vmax_varlen(w, vr, vmax_pos, plus=1),
+                      "valid sequences")
+        for i in (3, 17, 30, 39):   # only the new row: its V row, exactly
+            want = np.repeat(vn[i], hq // hkv, axis=0)
+            assert np.array_equal(out.cpu().numpy()[i], want), f"sequence {i}"
+    assert np.all(np.isnan(out.cpu().numpy()[5]))
+
+
 # ----------------------------------------------------------------- prefill
 
 def _gpu_prefill(dev, w, q, k, v, fill=float("nan")):
