@@ -103,7 +103,9 @@ attn_status attn_prefill_causal(const float *q, const float *k, const float *v,
  * Calls ordered on one stream may share one whatever their shapes while
  * batch * num_heads <= 16384 (all of them then have the same counter block);
  * beyond that, only calls of the same batch, num_heads, kv_heads and
- * head_dim, unless the workspace is zero-filled again in between.
+ * head_dim, unless the workspace is zero-filled again in between. A call
+ * that does not run to completion (a device fault) can leave counters set:
+ * zero-fill the workspace again before reusing it.
  */
 size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads,
                                    uint32_t kv_heads, uint32_t head_dim,
