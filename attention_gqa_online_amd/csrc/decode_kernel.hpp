@@ -57,7 +57,7 @@ struct DecodeArgs {
     // fused append (the merging workgroups): new rows [B, Hkv, D], or null
     const float *k_new;
     const float *v_new;
-    float *k_dst;     // the caches, written at row `position`
+    float *k_dst;     // the caches, written at the appended row (`position`, or per sequence)
     float *v_dst;
     uint32_t position;
     // rotary embedding of the current token (rotate-half), or null:
