@@ -770,6 +770,34 @@ def test_decode_append_varlen_units_without_rows(dev, rope):
     assert np.all(np.isnan(out.cpu().numpy()[5]))
 
 
+def test_decode_steps_deterministic_whichever_workgroup_merges(dev):
+    """The last workgroup of a unit to finish merges it, and which one that is
+    changes from call to call; the fold runs in split order all the same, so
+    repeated calls give the same bits: the decode step (many splits per unit)
+    and the varlen step, eight calls each on one workspace."""
+    b, hq, hkv, d, ms = 3, 12, 2, 128, 3000           # 6 units, 43 splits each
+    w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, ms, seed=51)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=52)
+    qd, knd, vnd = (torch.from_numpy(x).to(dev) for x in (q, kn, vn))
+    ws = A.decode_workspace(b, hq, hkv, d, ms, 0, device=dev)
+    pos = torch.from_numpy((synth.seq_lengths(b, ms, seed=53) - 1).astype(np.int32)).to(dev)
+    for varlen in (False, True):
+        outs = []
+        for _ in range(8):
+            kd, vd = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+            out = torch.empty(b, hq, d, device=dev)
+            if varlen:
+                A.attn_decode_append_varlen(qd, knd, vnd, kd, vd, out, pos, b, hq, hkv, d, ms, ms,
+                                            0, w.scale, ws)
+            else:
+                A.attn_decode_append(qd, knd, vnd, kd, vd, out, b, hq, hkv, d, ms, ms - 1, 0,
+                                     w.scale, ws)
+            outs.append(out)
+        torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0]), "varlen" if varlen else "uniform"
+
+
 # ----------------------------------------------------------------- prefill
 
 def _gpu_prefill(dev, w, q, k, v, fill=float("nan")):
