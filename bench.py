@@ -187,8 +187,9 @@ def bench_headline(args, dev):
     torch.cuda.synchronize()
     gwall = (time.perf_counter() - t0) * 1e3 / args.steps
     gev = g0.elapsed_time(g1) / args.steps
-    two["graph_replay_us_per_step"] = round(gwall * 1e3, 2)
-    two["graph_replay_event_us_per_step"] = round(gev * 1e3, 2)
+    graph = {"step": "attn_decode_append replayed from a captured HIP graph",
+             "us_per_step_wall": round(gwall * 1e3, 2),
+             "us_per_step_events": round(gev * 1e3, 2)}
     log(f"[bench] graph replay: {gwall * 1e3:.1f} us/step wall, {gev * 1e3:.1f} us by events")
     # the same step with rotary embedding (attn_decode_rope_append)
     cs = [torch.from_numpy(x).to(dev) for x in synth.rope_tables(w.head_dim, pos)]
@@ -200,12 +201,29 @@ def bench_headline(args, dev):
                                   w.kv_heads, w.head_dim, w.max_seq, pos, w.window, w.scale,
                                   wsp, wsb, stream=sint)
 
-    ms3, wall3 = time_calls(rope_step, args.steps, args.warmup, stream)
-    rope = {"step": "attn_decode_rope_append", "median_us": round(statistics.median(ms3) * 1e3, 2),
-            "wall_us_per_step": round(wall3 * 1e3, 2),
-            "GB/s": round(bytes_ / (statistics.median(ms3) * 1e-3) / 1e9, 1)}
-    log(f"[bench] rotary decode step: median {rope['median_us']:.1f} us")
-    return w, value, ms_per_step, roof, host_set0, two, rope
+    # timed as the headline step is: back to back between one event pair
+    # (per-call event pairs add host work per call, which can leave the GPU
+    # idle between calls and expose each dispatch)
+    for i in range(args.warmup):
+        rope_step(i)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(args.steps):
+        rope_step(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    rwall = (time.perf_counter() - t0) * 1e3 / args.steps
+    rev = r0.elapsed_time(r1) / args.steps
+    ms3, _ = time_calls(rope_step, args.steps, 0, stream)
+    rope = {"step": "attn_decode_rope_append", "us_per_step_events": round(rev * 1e3, 2),
+            "us_per_step_wall": round(rwall * 1e3, 2),
+            "median_us": round(statistics.median(ms3) * 1e3, 2),
+            "GB/s": round(bytes_ / (rev * 1e-3) / 1e9, 1)}
+    log(f"[bench] rotary decode step: {rev * 1e3:.1f} us/step by events, "
+        f"{rwall * 1e3:.1f} us/step wall (per-call median {rope['median_us']:.1f})")
+    return w, value, ms_per_step, roof, host_set0, two, rope, graph
 
 
 def cpu_baseline(w, host_set):
@@ -417,8 +435,8 @@ def main():
     dev = torch.device("cuda:0")
     modes = set(args.modes.split(","))
 
-    w, value, ms_per_step, roof, host_set, two, rope = bench_headline(args, dev)
-    extra = {"decode_step_two_calls": two, "decode_step_rope": rope}
+    w, value, ms_per_step, roof, host_set, two, rope, graph = bench_headline(args, dev)
+    extra = {"decode_step_two_calls": two, "decode_step_graph": graph, "decode_step_rope": rope}
     if "decode_window" in modes:
         extra["decode_window"] = bench_decode_window(args, dev)
     if "decode_varlen" in modes:
