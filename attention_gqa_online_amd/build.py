@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SO_PATH = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "kv_append.hip"]
+SOURCES = ["api.hip", "plan.cpp", "decode.hip", "prefill.hip", "kv_append.hip"]
 ARCH = "gfx950"
 
 

@@ -1,11 +1,39 @@
 // C ABI of libattn.so (declared in include/attn.h): argument checks on the
 // host, then one kernel launch on the caller's stream. No check below makes a
-// HIP call, so an invalid call returns before touching the device.
+// HIP call, so an invalid call returns before touching the device; the only
+// HIP calls before a launch are the once-per-device compute-unit query.
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "attn.h"
 #include "kernels.hpp"
+
+namespace attn {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_cus[kMaxDevices];  // 0: not queried yet
+}  // namespace
+
+uint32_t device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxCus;
+    if (dev < kMaxDevices) {
+        const uint32_t c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c != 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return kMaxCus;
+    const uint32_t c = (uint32_t)n < kMaxCus ? (uint32_t)n : kMaxCus;
+    if (dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+}  // namespace attn
 
 namespace {
 
@@ -15,6 +43,19 @@ bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 bool aligned4(const void *p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Host checks use the plan for kMaxCus compute units (plain arithmetic, no
+// HIP call); it needs at least the workspace and the workgroups of the plan
+// for any smaller count. Once they pass, the launch uses the plan for the
+// device's own count.
+attn::DecodePlan device_plan(const attn::DecodePlan &checked, uint32_t batch,
+                             uint32_t num_heads, uint32_t kv_heads, uint32_t head_dim,
+                             uint32_t total_seq, uint32_t window, bool append, bool varlen) {
+    const uint32_t cus = attn::device_cus();
+    if (cus >= attn::kMaxCus) return checked;
+    return attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window, append,
+                             varlen, cus);
+}
 
 }  // namespace
 
@@ -47,7 +88,9 @@ attn_status attn_prefill_causal(const float *q, const float *k, const float *v, 
     // waves 8 or 4
     const uint64_t pairs = (uint64_t)heads_per_kv * ((m + 31u) / 32u);
     if (kv_heads * ((pairs + 3) / 4) > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
-    return from_hip(attn::launch_prefill(q, k, v, o, m, q_stride, kv_stride, num_q_heads,
+    const attn::PrefillPlan plan =
+        attn::plan_prefill(m, num_q_heads, heads_per_kv, head_dim, attn::device_cus());
+    return from_hip(attn::launch_prefill(plan, q, k, v, o, m, q_stride, kv_stride, num_q_heads,
                                          heads_per_kv, head_dim, stream));
 }
 
@@ -57,12 +100,13 @@ size_t attn_decode_workspace_bytes(uint32_t batch, uint32_t num_heads, uint32_t 
     if (kv_heads == 0 || num_heads % kv_heads != 0 || total_seq == 0) return 0;
     if (batch == 0 || num_heads == 0) return 0;
     if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return 0;
-    // large enough for every decode entry point's plan of these shapes
+    // large enough for every decode entry point's plan of these shapes on
+    // any gfx950 device (plans on fewer compute units need no more)
     size_t need = 0;
     for (int append = 0; append < 2; ++append)
         for (int varlen = 0; varlen < 2; ++varlen) {
             const size_t n = attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq,
-                                               window, append != 0, varlen != 0)
+                                               window, append != 0, varlen != 0, attn::kMaxCus)
                                  .workspace_bytes;
             need = n > need ? n : need;
         }
@@ -83,10 +127,12 @@ attn_status attn_decode(const float *q, const float *k_cache, const float *v_cac
     if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return ATTN_ERR_INVALID;
-    const attn::DecodePlan plan =
-        attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window);
-    if (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_INVALID;
-    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodePlan chk = attn::plan_decode(batch, num_heads, kv_heads, head_dim,
+                                                   total_seq, window, false, false, attn::kMaxCus);
+    if (!aligned16(workspace) || workspace_bytes < chk.workspace_bytes) return ATTN_ERR_INVALID;
+    if ((uint64_t)chk.units * chk.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodePlan plan = device_plan(chk, batch, num_heads, kv_heads, head_dim,
+                                              total_seq, window, false, false);
     return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
                                         head_dim, max_seq, total_seq, scale, workspace,
                                         nullptr, stream));
@@ -148,7 +194,9 @@ attn_status decode_step(const float *q, const float *k_new, const float *v_new,
     if (!isfinite(scale)) return ATTN_ERR_INVALID;
     if (!head_dim_built(head_dim)) return ATTN_ERR_UNSUPPORTED;
     if (batch == 0) return ATTN_OK;
-    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if ((uint64_t)batch * kv_heads * num_heads > 0x7fffffffu ||
+        (uint64_t)batch * kv_heads * (head_dim / 4) > 0x7fffffffu)
+        return ATTN_ERR_UNSUPPORTED;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
         return ATTN_ERR_INVALID;
     if (num_heads == 0) {  // nothing to attend: the append alone
@@ -157,13 +205,15 @@ attn_status decode_step(const float *q, const float *k_new, const float *v_new,
                                                sin_t));
     }
     const uint32_t total_seq = position + 1;
-    const attn::DecodePlan plan =
-        attn::plan_decode(batch, num_heads, kv_heads, head_dim, total_seq, window, true);
+    const attn::DecodePlan chk = attn::plan_decode(batch, num_heads, kv_heads, head_dim,
+                                                   total_seq, window, true, false, attn::kMaxCus);
     attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, cos_t, sin_t};
     if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
-    if (plan.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes))
+    if (chk.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < chk.workspace_bytes))
         return ATTN_ERR_INVALID;
-    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if ((uint64_t)chk.units * chk.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodePlan plan = device_plan(chk, batch, num_heads, kv_heads, head_dim,
+                                              total_seq, window, true, false);
     return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
                                         head_dim, max_seq, total_seq, scale, workspace, &app,
                                         stream));
@@ -219,10 +269,12 @@ attn_status attn_decode_varlen(const float *q, const float *k_cache, const float
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         !aligned4(seq_lens))
         return ATTN_ERR_INVALID;
-    const attn::DecodePlan plan =
-        attn::plan_decode(batch, num_heads, kv_heads, head_dim, seq_bound, window, false, true);
-    if (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes) return ATTN_ERR_INVALID;
-    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodePlan chk = attn::plan_decode(batch, num_heads, kv_heads, head_dim,
+                                                   seq_bound, window, false, true, attn::kMaxCus);
+    if (!aligned16(workspace) || workspace_bytes < chk.workspace_bytes) return ATTN_ERR_INVALID;
+    if ((uint64_t)chk.units * chk.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodePlan plan = device_plan(chk, batch, num_heads, kv_heads, head_dim,
+                                              seq_bound, window, false, true);
     const attn::DecodeVarlen vl{seq_lens, 0, seq_bound, window};
     return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,
                                         head_dim, max_seq, seq_bound, scale, workspace,
@@ -259,11 +311,13 @@ attn_status decode_step_varlen(const float *q, const float *k_new, const float *
                                                sin_t, positions, cs_stride));
     }
     if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
-    const attn::DecodePlan plan =
-        attn::plan_decode(batch, num_heads, kv_heads, head_dim, seq_bound, window, true, true);
-    if (plan.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < plan.workspace_bytes))
+    const attn::DecodePlan chk = attn::plan_decode(batch, num_heads, kv_heads, head_dim,
+                                                   seq_bound, window, true, true, attn::kMaxCus);
+    if (chk.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < chk.workspace_bytes))
         return ATTN_ERR_INVALID;
-    if ((uint64_t)plan.units * plan.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if ((uint64_t)chk.units * chk.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    const attn::DecodePlan plan = device_plan(chk, batch, num_heads, kv_heads, head_dim,
+                                              seq_bound, window, true, true);
     const attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, cos_t, sin_t, cs_stride};
     const attn::DecodeVarlen vl{positions, 1, seq_bound, window};
     return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,

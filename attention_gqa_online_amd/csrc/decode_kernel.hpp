@@ -244,11 +244,32 @@ constexpr int kPartStride = D + 4;
 enum DecodeMerge { kMergeFused = 2, kMergeDirect = 3 };
 
 // Partial states that another workgroup of the same launch reads back go
-// through agent-scope (relaxed) atomic stores and loads, 8 bytes each: these
-// carry the device-scope cache bit (sc1), so a store is written through the
-// XCD's own L2 and acknowledged once every XCD can see it, and a load does
-// not take a line another XCD may have changed. No L2-wide writeback or
-// invalidate (what an agent-scope release/acquire fence costs) is needed.
+// through agent-scope (relaxed) atomic stores and loads, 8 bytes each.
+//
+// Why the merge needs no fence. The LLVM AMDGPU backend's user guide
+// (AMDGPUUsage, "Memory Model GFX942", whose code sequences the backend also
+// uses for gfx950) gives, for global memory at agent scope:
+//   - load atomic monotonic      -> global_load   ... sc1=1
+//   - store atomic monotonic     -> global_store  ... sc1=1
+//   - atomicrmw monotonic        -> global_atomic ... sc1=1
+//   - fence release              -> buffer_wbl2 sc1=1; s_waitcnt vmcnt(0)
+//   - fence acquire              -> s_waitcnt vmcnt(0); buffer_inv sc1=1
+// So an sc1 store is by itself coherent at agent scope (written through the
+// XCD's L2, and complete only once every XCD can see it), and an sc1 load by
+// itself reads the agent-coherent value (it never takes a line another XCD
+// may have changed). The release fence's buffer_wbl2 writes back what plain
+// stores left in the L2, and the acquire's buffer_inv drops what plain loads
+// could find stale there; the partial states are written and read only with
+// the sc1 accesses above, so neither is needed, and neither is issued (they
+// act on the XCD's whole L2 and measured 2-5x slower). What remains of the
+// release is its s_waitcnt vmcnt(0): every state store of the workgroup is
+// complete before the arrival counter moves (decode_fused_merge). What
+// remains of the acquire: the merging workgroup issues its state loads only
+// after the counter's returned value has arrived and passed through a
+// barrier, in program order. The compiler is kept from moving the accesses
+// across those points by signal fences (code-free compiler barriers). The
+// tests that poison the workspace before each call and that compare
+// repeated calls bit for bit guard this at run time.
 __device__ __forceinline__ void st_dev2(float *p, float x, float y) {
     const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) |
                        ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
@@ -333,9 +354,13 @@ __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerg
             st_dev2(ph + dv[it] + 2, num[it].z, num[it].w);
             if (dv[it] == 0) st_dev2(ph + D, M[it], den[it]);
         }
-        // every thread's stores are acknowledged before the barrier, and the
-        // count goes up only after it
+        // The release half (see st_dev2): every thread's sc1 stores are
+        // complete (s_waitcnt vmcnt(0)) before the barrier, and the count
+        // goes up only after it. The signal fences keep the compiler from
+        // moving a store below the wait or the counter above it.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __syncthreads();
         if (tid == 0) {
             const uint32_t prev =
@@ -345,6 +370,10 @@ __device__ __forceinline__ void decode_fused_merge(const DecodeArgs &a, SlotMerg
             s_last = last ? 1u : 0u;
         }
         __syncthreads();
+        // The acquire half: the state loads below (sc1) issue only after
+        // the counter's value came back and every thread saw it; the fence
+        // keeps the compiler from hoisting them above this point.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (s_last == 0) return;
     }
 
@@ -777,8 +806,5 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
         if (hh < nh) st4(a.out + ((size_t)b * a.num_heads + h0 + hh) * D + d, o);
     }
 }
-
-// Largest number of splits per unit the plan makes.
-constexpr int kMaxSplit = 1024;
 
 }  // namespace attn

@@ -6,30 +6,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "plan.hpp"
+
 namespace attn {
 
+// Compute units of the current device, queried once per device and cached
+// (kMaxCus where the query fails). Plans are made for this count.
+uint32_t device_cus();
+
 // ---------------------------------------------------------------- decode
-// Work split of one decode call: the attended rows [w0, total_seq) of every
-// (sequence, KV head, head chunk) unit are cut into n_split contiguous row
-// ranges of rows_per_split rows, one workgroup each.
-struct DecodePlan {
-    uint32_t head_chunk;      // Q heads handled per workgroup (<= 8)
-    uint32_t n_chunks;        // head chunks per KV head
-    uint32_t units;           // batch * kv_heads * n_chunks
-    uint32_t n_split;         // workgroups per unit
-    uint32_t rows_per_split;  // multiple of the rows one workgroup step covers
-    uint32_t w0;              // first attended row
-    size_t part_floats;       // partial-state floats in the workspace
-    size_t part_offset;       // bytes before them: the units' arrival counters
-    size_t workspace_bytes;   // counters + partial states (the whole workspace)
-};
-
-// With `append`, the split pass covers [w0, total_seq - 1) and the last row
-// comes from the new K/V rows instead (n_split may then be 0).
-DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
-                       uint32_t head_dim, uint32_t total_seq, uint32_t window,
-                       bool append = false, bool varlen = false);
-
 // New K/V rows for attn_decode_append: written at `position` = total_seq - 1;
 // with cos/sin ([D/2] for that position) q and the new K rows are rotated.
 // Per-sequence lengths for a batch of mixed lengths: T_b = lens[b] + len_add
@@ -59,9 +44,9 @@ hipError_t launch_decode(const DecodePlan &plan, const float *q, const float *k_
                          const DecodeVarlen *varlen = nullptr);
 
 // ---------------------------------------------------------------- prefill
-hipError_t launch_prefill(const float *q, const float *k, const float *v, float *o,
-                          uint32_t m, uint32_t q_stride, uint32_t kv_stride,
-                          uint32_t num_q_heads, uint32_t heads_per_kv,
+hipError_t launch_prefill(const PrefillPlan &plan, const float *q, const float *k,
+                          const float *v, float *o, uint32_t m, uint32_t q_stride,
+                          uint32_t kv_stride, uint32_t num_q_heads, uint32_t heads_per_kv,
                           uint32_t head_dim, hipStream_t stream);
 
 // ---------------------------------------------------------------- append

@@ -51,10 +51,9 @@ namespace {
 // head_dim registers, and with one wave per SIMD a lane has 512 registers
 // instead of 256, so nothing goes to scratch memory. (On smaller grids the
 // 4-wave workgroups would need two rounds of the CUs.)
-constexpr int kMinDim4Waves = 192;
-constexpr int kBr = 32;  // query rows per wave
+// (kMinDim4Waves and the grid itself: plan_prefill in plan.cpp)
+constexpr int kBr = kPrefillRows;  // query rows per wave
 constexpr int kBc = 64;  // keys per LDS tile
-constexpr int kCus = 256;  // compute units of an MI355X
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
 struct PrefillArgs {
@@ -389,9 +388,9 @@ hipError_t launch_d(const PrefillArgs &args, uint32_t grid, uint32_t nw, hipStre
 
 }  // namespace
 
-hipError_t launch_prefill(const float *q, const float *k, const float *v, float *o,
-                          uint32_t m, uint32_t q_stride, uint32_t kv_stride,
-                          uint32_t num_q_heads, uint32_t heads_per_kv,
+hipError_t launch_prefill(const PrefillPlan &plan, const float *q, const float *k,
+                          const float *v, float *o, uint32_t m, uint32_t q_stride,
+                          uint32_t kv_stride, uint32_t num_q_heads, uint32_t heads_per_kv,
                           uint32_t head_dim, hipStream_t stream) {
     PrefillArgs a{};
     a.q = q;
@@ -403,22 +402,13 @@ hipError_t launch_prefill(const float *q, const float *k, const float *v, float 
     a.kv_stride = kv_stride;
     a.hpk = heads_per_kv;
     a.kv_heads = num_q_heads / heads_per_kv;
-    const uint32_t n_rb = (m + kBr - 1) / kBr;
-    a.n_rb = n_rb;
-    a.n_pairs = heads_per_kv * n_rb;
-    uint32_t nw = 8;
-    if (head_dim >= kMinDim4Waves && (uint64_t)(a.n_pairs + 3) / 4 * a.kv_heads >= 2 * kCus)
-        nw = 4;
-    a.wg_per_group = (a.n_pairs + nw - 1) / nw;
-    // a grid under two workgroups per CU is bound by its heaviest workgroup:
-    // pair short and long row blocks instead
-    a.nsub = (heads_per_kv + nw / 2 - 1) / (nw / 2);
-    if ((uint64_t)a.wg_per_group * a.kv_heads < 2 * kCus) {
-        a.zigzag = 1;
-        a.wg_per_group = (n_rb + 1) / 2 * a.nsub;
-    }
+    a.n_rb = plan.n_rb;
+    a.n_pairs = plan.n_pairs;
+    a.wg_per_group = plan.wg_per_group;
+    a.zigzag = plan.zigzag;
+    a.nsub = plan.nsub;
     a.qscale = (1.0f / sqrtf((float)head_dim)) * kLog2e;
-    const uint32_t grid = a.wg_per_group * a.kv_heads;
+    const uint32_t grid = plan.grid, nw = plan.waves;
     switch (head_dim) {
     case 32: return launch_d<32>(a, grid, nw, stream);
     case 64: return launch_d<64>(a, grid, nw, stream);

@@ -1,9 +1,9 @@
 /*
  * attn.h -- fused grouped-query attention for AMD Instinct MI355X (gfx950).
  *
- * C ABI of libattn.so. Three operations (prefill and append are one kernel
- * launch each; decode is two, ordered on the caller's stream), and the decode
- * step that combines the last two:
+ * C ABI of libattn.so: three operations, the decode step that combines the
+ * last two, and their serving forms. Every entry point is one kernel launch
+ * on the caller's stream (decode merges its splits inside that launch):
  *
  *   attn_prefill_causal   causal self-attention over a packed projection output
  *   attn_decode           single-query attention over a KV cache, optional
@@ -32,7 +32,9 @@
  *   - Calls are asynchronous on `stream` (0 = the default stream). They
  *     return after the launch; errors inside the kernel surface at the
  *     caller's next synchronisation. All argument checks run on the host
- *     before any HIP call, so an invalid call launches nothing.
+ *     before any HIP call, so an invalid call launches nothing. The work
+ *     split follows the current device's compute-unit count, queried once
+ *     per device and kept for the life of the process.
  *   - Outputs must not overlap inputs. Concurrent calls must not share an
  *     output buffer or a decode workspace.
  *   - Pointers must be 16-byte aligned; strides are in elements and must be
@@ -93,7 +95,9 @@ attn_status attn_prefill_causal(const float *q, const float *k, const float *v,
 /*
  * Size in bytes of the decode workspace for these shapes (glia honeycrisp
  * "attention.rs" page: the decode module doc and its Params struct). Pure
- * host function; 0 if the shapes are invalid. Any device buffer at least this
+ * host function (no HIP call); 0 if the shapes are invalid. The size covers
+ * every decode entry point's work split on any gfx950 device (the split
+ * follows the device's compute units, at most 256). Any device buffer at least this
  * large serves, provided it was zero-filled before its first use (hipMemset,
  * a fill kernel, torch.zeros): it begins with a block of 32-bit arrival
  * counters, one per work unit, which every call leaves at zero again: the
@@ -173,8 +177,8 @@ attn_status attn_decode(const float *q, const float *k_cache,
  * (may be null when that size is 0).
  *
  * Errors: as attn_decode (with total_seq = position + 1), plus position >=
- * max_seq. batch == 0 returns ATTN_OK without a launch; num_heads == 0 only
- * appends.
+ * max_seq, and ATTN_ERR_UNSUPPORTED past kv_append's size bound. batch == 0
+ * returns ATTN_OK without a launch; num_heads == 0 only appends.
  */
 attn_status attn_decode_append(const float *q, const float *k_new, const float *v_new,
                                float *k_cache, float *v_cache, float *out,
@@ -235,8 +239,9 @@ attn_status attn_decode_rope_append(const float *q_raw, const float *k_raw,
  * element is written. Sources must not overlap the caches.
  *
  * Errors: ATTN_ERR_INVALID if head_dim % 32 != 0, position >= max_seq, or a
- * null / misaligned pointer. batch == 0 or kv_heads == 0 returns ATTN_OK
- * without a launch.
+ * null / misaligned pointer; ATTN_ERR_UNSUPPORTED if
+ * batch*kv_heads*head_dim/4 >= 2^31. batch == 0 or kv_heads == 0 returns
+ * ATTN_OK without a launch.
  */
 attn_status kv_append(const float *k_src, const float *v_src, float *k_cache,
                       float *v_cache, uint32_t batch, uint32_t kv_heads,

@@ -177,6 +177,11 @@ def test_decode_append_argument_rules(lib):
     assert _decode_append(lib, ws_bytes=0) == INVALID
     assert _decode_append(lib, ws=0) == INVALID
     assert _decode_append(lib, b=0) == OK                        # no work, no launch
+    # with no Q heads the step only appends: the append's own size bound
+    # (batch * kv_heads * head_dim / 4 < 2^31) still holds, as in kv_append
+    assert _decode_append(lib, b=1 << 24, hq=0, hkv=8, max_seq=1 << 20,
+                          pos=0) == UNSUPPORTED
+    assert lib.kv_append(P, P, P, P, 1 << 24, 8, 128, 1 << 20, 0, None) == UNSUPPORTED
 
 
 def _decode_rope(lib, b=2, hq=12, hkv=2, d=128, max_seq=64, pos=63, window=0,
@@ -200,6 +205,7 @@ def test_decode_rope_append_argument_rules(lib):
     assert _decode_rope(lib, ws=0) == INVALID
     assert _decode_rope(lib, b=0) == OK                            # no work, no launch
     assert _decode_rope(lib, b=0, ptrs=(0,) * 8) == OK
+    assert _decode_rope(lib, b=1 << 24, hq=0, hkv=8, max_seq=1 << 20, pos=0) == UNSUPPORTED
 
 
 def test_kv_append_rows_argument_rules(lib):
