@@ -31,18 +31,26 @@ SO_PATH = os.path.join(_HERE, "liboracle.so")
 # contraction, no host-specific ISA, so the .so runs on any x86-64 host.
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC",
           "-shared", "-Wall", "-Wextra"]
+# The build that is timed as the CPU baseline, on the host that runs it:
+# -O3 and that host's own ISA, still with no -ffast-math and no FMA
+# contraction, so every sum is evaluated as written, in index order.
+CFLAGS_NATIVE = ["-O3", "-march=native", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                 "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 _F32P = ctypes.POINTER(ctypes.c_float)
 _U32P = ctypes.POINTER(ctypes.c_uint32)
 _F64P = ctypes.POINTER(ctypes.c_double)
 
 
-def build(force: bool = True, src: str = _SRC, so_path: str = SO_PATH) -> str:
-    """Compile oracle.c (or another copy of it) into a shared library."""
+def build(force: bool = True, src: str = _SRC, so_path: str = SO_PATH,
+          native: bool = False) -> str:
+    """Compile oracle.c (or another copy of it) into a shared library;
+    ``native`` builds with CFLAGS_NATIVE for the host it runs on."""
     global _default
     if force or not os.path.exists(so_path):
         tmp = so_path + ".tmp"
-        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, src, "-lm"])
+        flags = CFLAGS_NATIVE if native else CFLAGS
+        subprocess.check_call(["gcc", *flags, "-o", tmp, src, "-lm"])
         os.replace(tmp, so_path)
         if so_path == SO_PATH:
             _default = None

@@ -35,3 +35,39 @@ def test_traffic_is_reported_only_for_the_measured_sources(tmp_path, monkeypatch
     assert bench.measured_traffic("missing") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
     assert bench.measured_traffic("k_now") is None
+
+
+def test_host_info_names_the_cpu():
+    h = bench.host_info()
+    assert h["nproc"] >= 1 and h["affinity_cpus"] >= 1
+    assert h["cpu_model"]
+
+
+def test_cpu_oracle_is_built_for_this_host_and_timed():
+    """The CPU baseline's oracle: a native -O3 build of the same oracle.c,
+    giving the same numbers as the portable build the tests use."""
+    import numpy as np
+    import oracle
+    import synth
+    orc = bench.CpuOracle(bench.host_info())
+    assert orc.threads >= 1
+    w = synth.WORKLOADS["prefill_hq4_hkv2_d32_m16"]
+    q, k, v = synth.prefill_inputs(w)
+    args = (q, k, v, w.m, w.q_stride, w.kv_stride, w.num_q_heads, w.heads_per_kv, w.head_dim)
+    out, ts = orc.time(lambda: orc.o.prefill_causal(*args), reps=3)
+    assert len(ts) >= 3 and min(ts) > 0
+    ref = oracle.prefill_causal(*args)
+    # both builds evaluate every sum in the same order without contraction
+    assert np.array_equal(out, ref)
+    rec = orc.record(w.flops(), 1e9, "GFLOP/s", ts, "test")
+    assert rec["kind"] == "oracle" and rec["cores"] == orc.threads and rec["value"] > 0
+    assert rec["cpu_model"] and rec["nproc"] >= 1
+
+
+def test_parity_bound():
+    import numpy as np
+    ref = np.array([1.0, -2.0, 3.0])
+    p = bench.parity(np.array([1.0, -2.0, 3.0], np.float32), ref, 4.0)
+    assert p["ok"] and p["max_abs_err"] == 0.0
+    p = bench.parity(np.array([1.0, -2.0, 3.001], np.float32), ref, 4.0)
+    assert not p["ok"] and p["bound"] == bench.TOL * 4.0
