@@ -87,6 +87,14 @@ def library() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{SO_PATH} is missing: build it with "
                 "`python -m attention_gqa_online_amd.build` (hipcc, gfx950)")
+        # torch first: it loads its own HIP runtime (soname libamdhip64.so.7,
+        # the name libattn.so asks for), so the library binds to that same
+        # runtime. Loaded the other way round, the process would hold two
+        # HIP runtimes, and the second to start finds no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(SO_PATH)
         lib.attn_prefill_causal.restype = ctypes.c_int
         lib.attn_prefill_causal.argtypes = [_vp, _vp, _vp, _vp, _u32, _u32, _u32,
