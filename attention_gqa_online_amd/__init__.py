@@ -24,6 +24,9 @@ import still succeeds, but the first call raises.
                             v_cache, out, batch, num_heads, kv_heads,
                             head_dim, max_seq, position, window, scale,
                             workspace, workspace_bytes=None, stream=None)
+    attn_decode_append_noalloc(q, k_new, v_new, k_cache, v_cache, out, batch,
+                               num_heads, kv_heads, head_dim, max_seq,
+                               position, window, scale, stream=None)
     kv_append_rows(k_src, v_src, k_cache, v_cache, m, kv_stride, kv_heads,
                    head_dim, max_seq, position, stream=None)
     attn_decode_varlen(q, k_cache, v_cache, out, seq_lens, batch, num_heads,
@@ -53,7 +56,8 @@ __all__ = [
     "AttnError", "ATTN_OK", "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED",
     "ATTN_ERR_HIP", "SO_PATH", "library", "attn_prefill_causal",
     "attn_decode_workspace_bytes", "attn_decode", "kv_append",
-    "attn_decode_append", "attn_decode_rope_append", "kv_append_rows",
+    "attn_decode_append", "attn_decode_rope_append", "attn_decode_append_noalloc",
+    "kv_append_rows",
     "attn_decode_varlen", "attn_decode_append_varlen", "attn_decode_rope_append_varlen",
     "attn_status_string", "decode_workspace",
 ]
@@ -64,6 +68,7 @@ ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 
 EXPORTS = ("attn_prefill_causal", "attn_decode_workspace_bytes", "attn_decode",
            "kv_append", "attn_decode_append", "attn_decode_rope_append",
+           "attn_decode_append_noalloc",
            "kv_append_rows", "attn_decode_varlen", "attn_decode_append_varlen",
            "attn_decode_rope_append_varlen", "attn_status_string")
 
@@ -115,6 +120,8 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_rope_append.restype = ctypes.c_int
         lib.attn_decode_rope_append.argtypes = [_vp] * 8 + [_u32] * 7 + [
             ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        lib.attn_decode_append_noalloc.restype = ctypes.c_int
+        lib.attn_decode_append_noalloc.argtypes = [_vp] * 6 + [_u32] * 7 + [ctypes.c_float, _vp]
         lib.kv_append_rows.restype = ctypes.c_int
         lib.kv_append_rows.argtypes = [_vp] * 4 + [_u32] * 6 + [_vp]
         lib.attn_decode_varlen.restype = ctypes.c_int
@@ -279,6 +286,22 @@ def attn_decode_rope_append(q_raw, k_raw, v_raw, cos_t, sin_t, k_cache, v_cache,
         batch, num_heads, kv_heads, head_dim, max_seq, position, window, float(scale),
         _ptr(workspace, "workspace"), int(workspace_bytes), _stream(stream))
     _check("attn_decode_rope_append", st)
+
+
+def attn_decode_append_noalloc(q, k_new, v_new, k_cache, v_cache, out, batch, num_heads,
+                               kv_heads, head_dim, max_seq, position, window, scale,
+                               stream=None) -> None:
+    """attn_decode_append with the library's own per-GPU workspace array (no
+    workspace argument, nothing allocated); calls on one GPU must not overlap."""
+    n_src = batch * kv_heads * head_dim
+    n_cache = batch * kv_heads * max_seq * head_dim
+    st = library().attn_decode_append_noalloc(
+        _ptr(q, "q", batch * num_heads * head_dim), _ptr(k_new, "k_new", n_src),
+        _ptr(v_new, "v_new", n_src), _ptr(k_cache, "k_cache", n_cache),
+        _ptr(v_cache, "v_cache", n_cache), _ptr(out, "out", batch * num_heads * head_dim),
+        batch, num_heads, kv_heads, head_dim, max_seq, position, window, float(scale),
+        _stream(stream))
+    _check("attn_decode_append_noalloc", st)
 
 
 def kv_append_rows(k_src, v_src, k_cache, v_cache, m, kv_stride, kv_heads, head_dim,

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "attn.h"
 #include "kernels.hpp"
@@ -36,6 +37,58 @@ uint32_t device_cus() {
 }  // namespace attn
 
 namespace {
+
+// ---- the decode workspace of attn_decode_append_noalloc: one array per GPU
+// (each device holds its own copy of this file-scope array from the moment
+// the library's code is loaded on it until the process ends). Layout as any
+// decode workspace: the fixed block of arrival counters (which every
+// complete call leaves at zero), then partial states. Calls on one GPU all
+// use it, so calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, per device, and only that
+// address is ever passed to a kernel.
+struct ScratchSlot {
+    bool ready;
+    void *ptr;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kScratchDevices];
+
+__global__ void clear_words_kernel(uint32_t *p, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// This GPU's scratch address. On the first call on a device (with it
+// current) the address is looked up and the counter block cleared on
+// `stream`, ahead of the call's own kernel (static device memory starts at
+// zero as well; the clear makes that explicit). Nothing is allocated.
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchSlot &slot = g_scratch[dev];
+    if (!slot.ready) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        constexpr uint32_t words = attn::kCounterBlock / sizeof(uint32_t);
+        hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(p), words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        slot.ptr = p;
+        slot.ready = true;
+    }
+    *out = slot.ptr;
+    return hipSuccess;
+}
 
 bool head_dim_multiple_of_32(uint32_t d) { return d != 0 && d % 32 == 0; }
 bool head_dim_built(uint32_t d) { return d >= 32 && d <= 256 && d % 32 == 0; }
@@ -147,7 +200,7 @@ attn_status decode_step(const float *q, const float *k_new, const float *v_new,
                         float *v_cache, float *out, uint32_t batch, uint32_t num_heads,
                         uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
                         uint32_t position, uint32_t window, float scale, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+                        size_t workspace_bytes, hipStream_t stream, bool use_scratch = false);
 
 }  // namespace
 
@@ -178,16 +231,29 @@ attn_status attn_decode_rope_append(const float *q_raw, const float *k_raw,
                        workspace, workspace_bytes, stream);
 }
 
+attn_status attn_decode_append_noalloc(const float *q, const float *k_new, const float *v_new,
+                                       float *k_cache, float *v_cache, float *out,
+                                       uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
+                                       uint32_t head_dim, uint32_t max_seq, uint32_t position,
+                                       uint32_t window, float scale, hipStream_t stream) {
+    return decode_step(q, k_new, v_new, nullptr, nullptr, k_cache, v_cache, out, batch,
+                       num_heads, kv_heads, head_dim, max_seq, position, window, scale, nullptr,
+                       0, stream, true);
+}
+
 }  // extern "C"
 
 namespace {
 
+// use_scratch: the workspace is this GPU's scratch array (above) instead of
+// the caller's buffer; shapes whose plan needs more than it holds, or more
+// arrival counters than its fixed counter block, are ATTN_ERR_UNSUPPORTED.
 attn_status decode_step(const float *q, const float *k_new, const float *v_new,
                         const float *cos_t, const float *sin_t, float *k_cache,
                         float *v_cache, float *out, uint32_t batch, uint32_t num_heads,
                         uint32_t kv_heads, uint32_t head_dim, uint32_t max_seq,
                         uint32_t position, uint32_t window, float scale, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, hipStream_t stream, bool use_scratch) {
     if (!head_dim_multiple_of_32(head_dim) || kv_heads == 0) return ATTN_ERR_INVALID;
     if (num_heads % kv_heads != 0) return ATTN_ERR_INVALID;
     if (position >= max_seq) return ATTN_ERR_INVALID;
@@ -209,9 +275,18 @@ attn_status decode_step(const float *q, const float *k_new, const float *v_new,
                                                    total_seq, window, true, false, attn::kMaxCus);
     attn::DecodeAppend app{k_new, v_new, k_cache, v_cache, cos_t, sin_t};
     if (!aligned16(q) || !aligned16(out)) return ATTN_ERR_INVALID;
-    if (chk.workspace_bytes > 0 && (!aligned16(workspace) || workspace_bytes < chk.workspace_bytes))
+    if (use_scratch) {
+        if (chk.workspace_bytes > kScratchBytes || chk.part_offset > attn::kCounterBlock)
+            return ATTN_ERR_UNSUPPORTED;
+    } else if (chk.workspace_bytes > 0 &&
+               (!aligned16(workspace) || workspace_bytes < chk.workspace_bytes)) {
         return ATTN_ERR_INVALID;
+    }
     if ((uint64_t)chk.units * chk.n_split > 0x7fffffffu) return ATTN_ERR_UNSUPPORTED;
+    if (use_scratch && chk.workspace_bytes > 0) {
+        const hipError_t e = scratch_address(stream, &workspace);
+        if (e != hipSuccess) return ATTN_ERR_HIP;
+    }
     const attn::DecodePlan plan = device_plan(chk, batch, num_heads, kv_heads, head_dim,
                                               total_seq, window, true, false);
     return from_hip(attn::launch_decode(plan, q, k_cache, v_cache, out, num_heads, kv_heads,

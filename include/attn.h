@@ -14,6 +14,9 @@
  *   attn_decode_rope_append
  *                         the same decode step with rotary position embedding
  *                         applied to q and to the new K rows on the way in
+ *   attn_decode_append_noalloc
+ *                         attn_decode_append without a workspace argument,
+ *                         for callers that cannot allocate
  *   kv_append_rows        write a prefill pass's K and V rows into a
  *                         sequence's caches (prefill -> decode hand-over)
  *   attn_decode_varlen    attn_decode with one length per sequence
@@ -227,6 +230,37 @@ attn_status attn_decode_rope_append(const float *q_raw, const float *k_raw,
                                     uint32_t position, uint32_t window,
                                     float scale, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_decode_append for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.
+ * The same step and kernels, with the decode workspace taken from a 16 MiB
+ * array inside the library instead of a caller's buffer.
+ *
+ * Arguments and results: as attn_decode_append, without workspace and
+ * workspace_bytes. The array is per GPU: each device the library runs on
+ * holds its own copy until the process ends. The first call on a device
+ * looks up that device's copy and clears its arrival counters on `stream`;
+ * no call allocates or frees memory.
+ *
+ * Every call on one GPU uses that GPU's array (and leaves its counters at
+ * zero), so calls that overlap on one GPU race: order them on one stream. A
+ * call that does not run to completion (a device fault) leaves the array
+ * unusable for the rest of the process.
+ *
+ * Errors: as attn_decode_append, plus ATTN_ERR_UNSUPPORTED when the step's
+ * work split needs more than the 16 MiB (the batch of 32 sequences x 12 Q /
+ * 2 KV heads of 128 needs under 1 MiB at any position) or more than 16384
+ * work units (batch * kv_heads * ceil(num_heads / kv_heads / 8)), and
+ * ATTN_ERR_HIP if the array's device address cannot be looked up.
+ */
+attn_status attn_decode_append_noalloc(const float *q, const float *k_new,
+                                       const float *v_new, float *k_cache,
+                                       float *v_cache, float *out, uint32_t batch,
+                                       uint32_t num_heads, uint32_t kv_heads,
+                                       uint32_t head_dim, uint32_t max_seq,
+                                       uint32_t position, uint32_t window, float scale,
+                                       hipStream_t stream);
 
 /*
  * KV-cache append of K and V in one launch (glia honeycrisp "attention.rs"
