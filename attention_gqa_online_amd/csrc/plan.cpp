@@ -90,6 +90,15 @@ PrefillPlan plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv
     if ((uint64_t)p.wg_per_group * kv_heads < 2ull * cus) {
         p.zigzag = 1;
         p.wg_per_group = (p.n_rb + 1) / 2 * p.nsub;
+        if (head_dim >= (uint32_t)kMinDim4Waves && head_dim % 64 == 0 && p.waves == 8) {
+            // 16-row blocks, a pair per wave: equal work for every wave, and
+            // half the registers of a 32-row block (the 8-wave 32-row kernel
+            // spills at these head sizes)
+            p.rows16 = 1;
+            p.n_rb16 = (m + 15) / 16;
+            p.n_tasks16 = (p.n_rb16 + 1) / 2 * heads_per_kv;
+            p.wg_per_group = (p.n_tasks16 + 7) / 8;
+        }
     }
     p.grid = p.wg_per_group * kv_heads;
     return p;

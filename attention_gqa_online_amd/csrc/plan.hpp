@@ -88,7 +88,11 @@ constexpr int kMinDim4Waves = 192;     // head_dim from which large grids use 4-
 // row-block-major (wave w of workgroup i owns (row block, head) pair
 // i*waves + w of its group), or, on grids under two workgroups per compute
 // unit, zigzag (the first half of the waves take row block u, the second
-// half row block n_rb-1-u, nsub workgroups per pair of row blocks).
+// half row block n_rb-1-u, nsub workgroups per pair of row blocks). Zigzag
+// grids of head_dim 192 or 256 use 16-row blocks instead (rows16): every
+// wave takes the 16-row blocks u and n_rb16-1-u of one head, one after the
+// other, so all waves carry the same work; task t = u * heads_per_kv + head
+// of a KV head's list goes to wave t mod 8 of its workgroup t / 8.
 struct PrefillPlan {
     uint32_t waves;         // 8, or 4 for head_dim >= kMinDim4Waves on large grids
     uint32_t n_rb;          // ceil(m / 32)
@@ -97,6 +101,9 @@ struct PrefillPlan {
     uint32_t nsub;          // zigzag: workgroups per row-block pair
     uint32_t wg_per_group;  // workgroups per KV head
     uint32_t grid;          // wg_per_group * kv_heads
+    uint32_t rows16;        // 1: the 16-row kernel (then the fields below)
+    uint32_t n_rb16;        // ceil(m / 16)
+    uint32_t n_tasks16;     // ceil(n_rb16 / 2) * heads_per_kv per KV head
 };
 
 PrefillPlan plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv,

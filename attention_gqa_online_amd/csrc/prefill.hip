@@ -67,6 +67,8 @@ struct PrefillArgs {
     uint32_t n_rb;         // ceil(m / 32)
     uint32_t zigzag;       // 1: waves 0-3 / 4-7 take row blocks u / n_rb-1-u
     uint32_t nsub;         // zigzag: workgroups per row-block pair (ceil(hpk / (waves / 2)))
+    uint32_t n_rb16;       // 16-row kernel: ceil(m / 16)
+    uint32_t n_tasks16;    // 16-row kernel: ceil(n_rb16 / 2) * hpk per KV head
     float qscale;          // (1/sqrt(d) in f32) * log2(e)
 };
 
@@ -374,8 +376,289 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-row variant for grids under two workgroups per CU at head_dim 192 and
+// 256 (v_mfma_f32_16x16x4_f32).
+//
+// There the 8-wave 32-row kernel needs head_dim registers per lane for Q^T
+// and O^T alone and spills to scratch; a 16-row block needs half. The zigzag
+// pairs of that kernel (short and long block on one SIMD) also leave the
+// long wave running alone for the last tiles. Here a wave owns the 16-row
+// blocks u and n_rb16-1-u of one head and runs them one after the other, so
+// every wave carries the same number of tile steps and both waves of a SIMD
+// stay busy to the end. The 8 waves of a workgroup take 8 consecutive tasks
+// (u, head) of one KV head, so their row blocks differ by at most one tile
+// and they still share every K/V tile in LDS: the workgroup streams the
+// tiles of the first blocks, then, from tile 0 again, those of the second.
+//
+// Operand layouts of 16x16x4 f32: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16] and receives C[4(l/16) + v][l%16] in register v. With
+// i = j = l%16 and kq = l/16:
+//   S^T[64 keys x 16 rows] = K_tile . Q^T: four 16-key blocks kb; k-step
+//     (g, c) uses d = 16g + 4kq + c, so a lane reads K[key][16g+4kq .. +3]
+//     with one ds_read_b128 and holds Q[row j][16g+4kq .. +3] in registers.
+//     Register v of block kb holds S^T[16kb + 4kq + v][row j].
+//   O^T[D x 16 rows] += V_tile^T . P^T: k-step (kb, v) takes keys
+//     16kb + 4kq + v, so its B operand is S^T register (kb, v) as it is; output
+//     block mb = 4q + c holds d = 64q + 4i + c, so a lane reads the 16-byte
+//     chunks i and 16 + i, ... of a V row (16 lanes: 256 contiguous bytes).
+// Needs head_dim a multiple of 64. (At head_dim 128 it measured slower than
+// the 32-row kernel: its per-step overheads weigh twice as much per FLOP.)
 template <int D>
-hipError_t launch_d(const PrefillArgs &args, uint32_t grid, uint32_t nw, hipStream_t stream) {
+__global__ __launch_bounds__(512) void prefill16_kernel(PrefillArgs a) {
+    constexpr int NW = 8;
+    constexpr int NG = D / 16;   // float4 of the Q^T operand per lane
+    constexpr int NQ4 = D / 64;  // 16-byte V chunks per lane per key
+    constexpr int NMB = D / 16;  // 16-row blocks of O^T
+    constexpr int NBUF = D <= 128 ? 2 : 1;
+    constexpr int TILE = kBc * D;
+    static_assert(D % 64 == 0, "head_dim a multiple of 64");
+    __shared__ __attribute__((aligned(16))) float sK0[TILE];
+    __shared__ __attribute__((aligned(16))) float sV0[TILE];
+    __shared__ __attribute__((aligned(16))) float sK1[NBUF == 2 ? TILE : 4];
+    __shared__ __attribute__((aligned(16))) float sV1[NBUF == 2 ? TILE : 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;   // query row of this lane (and A-operand row i)
+    const int kq = lane >> 4;  // k lane group
+
+    const uint32_t g = blockIdx.x % a.kv_heads;
+    const uint32_t wi = blockIdx.x / a.kv_heads;
+    const uint32_t t = wi * NW + wave;
+    const bool active = t < a.n_tasks16;
+    const uint32_t tt = active ? t : a.n_tasks16 - 1;  // idle waves: in bounds, no store
+    const uint32_t u = tt / a.hpk;
+    const uint32_t h = g * a.hpk + tt % a.hpk;
+    const uint32_t rbA = u, rbB = a.n_rb16 - 1 - u;  // rbB == rbA: the middle block, once
+
+    // 64-key tiles a 16-row block needs: keys [0, min(16 rb + 16, m))
+    auto tiles_of = [&](uint32_t rb) { return (min(16 * rb + 16, a.m) + kBc - 1) / kBc; };
+    const uint32_t t_first = wi * NW;
+    const uint32_t t_last = min(t_first + NW - 1, a.n_tasks16 - 1);
+    const uint32_t uA = t_last / a.hpk;  // largest first block of the workgroup
+    const uint32_t uB = t_first / a.hpk; // largest second block: a.n_rb16 - 1 - uB
+    const uint32_t ntA = tiles_of(uA);
+    const uint32_t ntB = a.n_rb16 - 1 - uB != uB ? tiles_of(a.n_rb16 - 1 - uB) : 0;
+    const uint32_t my_ntA = active ? tiles_of(rbA) : 0;
+    const uint32_t my_ntB = active && rbB != rbA ? tiles_of(rbB) : 0;
+
+    float4 qt[NG];
+    floatx4 acc[NMB];
+    float mrow, lrow;
+    uint32_t qr0 = 0, my_nt = 0;
+
+    // start a block: Q^T operand (pre-scaled; zero past m), cleared state
+    auto begin = [&](uint32_t rb, uint32_t nt) {
+        qr0 = rb * 16;
+        my_nt = nt;
+        const uint32_t qi = qr0 + j;
+        const bool ok = nt > 0 && qi < a.m;
+        const float *qrow = a.q + (size_t)(ok ? qi : 0) * a.q_stride + (size_t)h * D + 4 * kq;
+        const float qs = ok ? a.qscale : 0.f;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) qt[gg] = ld4(qrow + 16 * gg) * qs;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mb][v] = 0.f;
+        mrow = kNegInf;
+        lrow = 0.f;
+    };
+    // finish a block: normalise and store rows qr0 + j < m
+    auto finish = [&]() {
+        if (my_nt == 0) return;
+        float l = lrow + __shfl_xor(lrow, 16);
+        l += __shfl_xor(l, 32);
+        const uint32_t qi = qr0 + j;
+        if (qi >= a.m) return;
+        const float inv = 1.0f / l;
+        float *orow = a.o + (size_t)qi * a.q_stride + (size_t)h * D + 16 * kq;
+#pragma unroll
+        for (int q = 0; q < NQ4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                st4(orow + 64 * q + 4 * v,
+                    make_float4(acc[4 * q + 0][v] * inv, acc[4 * q + 1][v] * inv,
+                                acc[4 * q + 2][v] * inv, acc[4 * q + 3][v] * inv));
+    };
+
+    // matrix work of one tile (sk, sv in LDS) for this wave's current block
+    auto tile = [&](const float *sk, const float *sv, uint32_t kt) {
+        if (kt >= my_nt) return;  // wave-uniform
+        int xj = j;
+        asm volatile("" : "+v"(xj));  // swizzle key formed at each use, not held
+        floatx4 s[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s[kb][v] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
+        {
+            // step gg: the four 16-key blocks' K chunks (rows 16kb + i, whose
+            // swizzle key is i), read one step ahead; the four accumulator
+            // chains interleave so no MFMA waits on the one before it
+            const float *krow = sk + xj * D;
+            float4 ka[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                ka[0][kb] = ld4(krow + 16 * kb * D + 4 * swz_chunk<D>(xj, kq));
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                if (gg + 1 < NG) {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        ka[(gg + 1) & 1][kb] =
+                            ld4(krow + 16 * kb * D + 4 * swz_chunk<D>(xj, 4 * (gg + 1) + kq));
+                }
+                const float4 *kc = ka[gg & 1];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[kb].x, qt[gg].x, s[kb], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[kb].y, qt[gg].y, s[kb], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[kb].z, qt[gg].z, s[kb], 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[kb].w, qt[gg].w, s[kb], 0, 0, 0);
+            }
+            // keep that order through scheduling: the reads of step gg + 1
+            // go ahead of the 16 MFMAs of step gg
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads of steps 0, 1
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs of step gg
+                if (gg + 2 < NG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of gg + 2
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+
+        const uint32_t qi = qr0 + j;
+        // causal mask on tiles that reach past this block's first row (also
+        // removes the re-read rows past m: their keys exceed every query)
+        if (kt * kBc + kBc - 1 > qr0) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (kt * kBc + 16 * kb + 4 * kq + v > qi) s[kb][v] = kNegInf;
+        }
+        // online softmax for row qi: its 64 scores sit in lanes j, j+16,
+        // j+32, j+48, 16 each; every processed tile has an unmasked key per row
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (__any(mx > mrow + kLazyRescale)) {  // wave-uniform, as in prefill_kernel
+            const float mnew = fmaxf(mrow, mx);
+            const float cf = fast_exp2(mrow - mnew);
+            mrow = mnew;
+            lrow *= cf;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[mb][v] *= cf;
+        }
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                s[kb][v] = fast_exp2(s[kb][v] - mrow);
+                ls += s[kb][v];
+            }
+        lrow += ls;
+
+        __builtin_amdgcn_s_setprio(1);
+        {
+            // k-step e = (kb, v) takes keys 16kb + 4kq + v; its V chunks are
+            // read one step ahead of its MFMAs
+            auto vload = [&](int e, float4 (&vv)[NQ4]) {
+                const int key = 16 * (e >> 2) + 4 * kq + (e & 3);
+                const float *vrow = sv + key * D;
+#pragma unroll
+                for (int q = 0; q < NQ4; ++q) vv[q] = ld4(vrow + 4 * swz_chunk<D>(key, 16 * q + xj));
+            };
+            float4 vv[2][NQ4];
+            vload(0, vv[0]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                if (e + 1 < 16) vload(e + 1, vv[(e + 1) & 1]);
+                const float p = s[e >> 2][e & 3];
+#pragma unroll
+                for (int q = 0; q < NQ4; ++q) {
+                    const float4 x = vv[e & 1][q];
+                    acc[4 * q + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, p, acc[4 * q + 0], 0, 0, 0);
+                    acc[4 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, p, acc[4 * q + 1], 0, 0, 0);
+                    acc[4 * q + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, p, acc[4 * q + 2], 0, 0, 0);
+                    acc[4 * q + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, p, acc[4 * q + 3], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NQ4, 0);  // reads of k-steps 0, 1
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * NQ4, 0);  // MFMAs of k-step e
+                if (e + 2 < 16) __builtin_amdgcn_sched_group_barrier(0x100, NQ4, 0);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // the workgroup's tile stream: it = 0 .. ntA-1 are tiles 0.. of the
+    // first blocks, it = ntA .. ntA+ntB-1 tiles 0.. of the second blocks
+    const uint32_t nit = ntA + ntB;
+    auto kt_of = [&](uint32_t it) { return it < ntA ? it : it - ntA; };
+    begin(rbA, my_ntA);
+    if (nit > 0) load_tile_lds<D, NW>(a, g, 0, sK0, sV0, wave, lane);
+    auto step = [&](uint32_t it, const float *sk, const float *sv) {
+        if (it == ntA) {  // second blocks start
+            finish();
+            begin(rbB, my_ntB);
+        }
+        tile(sk, sv, kt_of(it));
+    };
+    if constexpr (NBUF == 2) {
+        for (uint32_t it = 0; it < nit; it += 2) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile it landed
+            __syncthreads();                     // every wave's loads landed; buffer 1 is free
+            if (it + 1 < nit) load_tile_lds<D, NW>(a, g, kt_of(it + 1), sK1, sV1, wave, lane);
+            step(it, sK0, sV0);
+            if (it + 1 >= nit) break;
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();  // buffer 0 is free
+            if (it + 2 < nit) load_tile_lds<D, NW>(a, g, kt_of(it + 2), sK0, sV0, wave, lane);
+            step(it + 1, sK1, sV1);
+        }
+    } else {
+        for (uint32_t it = 0; it < nit; ++it) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            step(it, sK0, sV0);
+            if (it + 1 < nit) {
+                __syncthreads();  // single buffer: everyone done before it is refilled
+                load_tile_lds<D, NW>(a, g, kt_of(it + 1), sK0, sV0, wave, lane);
+            }
+        }
+    }
+    finish();  // the second blocks (or the first, in a workgroup without second blocks)
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs &args, uint32_t grid, uint32_t nw, bool rows16,
+                    hipStream_t stream) {
+    if constexpr (D >= kMinDim4Waves && D % 64 == 0) {  // the plan's rows16 head sizes
+        if (rows16) {
+            hipLaunchKernelGGL((prefill16_kernel<D>), dim3(grid), dim3(8 * 64), 0, stream, args);
+            return hipGetLastError();
+        }
+    }
     if constexpr (D >= kMinDim4Waves) {
         if (nw == 4) {
             hipLaunchKernelGGL((prefill_kernel<D, 4>), dim3(grid), dim3(4 * 64), 0, stream, args);
@@ -407,17 +690,20 @@ hipError_t launch_prefill(const PrefillPlan &plan, const float *q, const float *
     a.wg_per_group = plan.wg_per_group;
     a.zigzag = plan.zigzag;
     a.nsub = plan.nsub;
+    a.n_rb16 = plan.n_rb16;
+    a.n_tasks16 = plan.n_tasks16;
     a.qscale = (1.0f / sqrtf((float)head_dim)) * kLog2e;
     const uint32_t grid = plan.grid, nw = plan.waves;
+    const bool r16 = plan.rows16 != 0;
     switch (head_dim) {
-    case 32: return launch_d<32>(a, grid, nw, stream);
-    case 64: return launch_d<64>(a, grid, nw, stream);
-    case 96: return launch_d<96>(a, grid, nw, stream);
-    case 128: return launch_d<128>(a, grid, nw, stream);
-    case 160: return launch_d<160>(a, grid, nw, stream);
-    case 192: return launch_d<192>(a, grid, nw, stream);
-    case 224: return launch_d<224>(a, grid, nw, stream);
-    case 256: return launch_d<256>(a, grid, nw, stream);
+    case 32: return launch_d<32>(a, grid, nw, r16, stream);
+    case 64: return launch_d<64>(a, grid, nw, r16, stream);
+    case 96: return launch_d<96>(a, grid, nw, r16, stream);
+    case 128: return launch_d<128>(a, grid, nw, r16, stream);
+    case 160: return launch_d<160>(a, grid, nw, r16, stream);
+    case 192: return launch_d<192>(a, grid, nw, r16, stream);
+    case 224: return launch_d<224>(a, grid, nw, r16, stream);
+    case 256: return launch_d<256>(a, grid, nw, r16, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -28,7 +28,8 @@ void probe_plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
     out[9] = p.workspace_bytes;
 }
 
-// out: waves, n_rb, n_pairs, zigzag, nsub, wg_per_group, grid
+// out: waves, n_rb, n_pairs, zigzag, nsub, wg_per_group, grid, rows16, n_rb16,
+// n_tasks16
 void probe_plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv,
                         uint32_t head_dim, uint32_t cus, uint64_t *out) {
     const attn::PrefillPlan p =
@@ -40,6 +41,9 @@ void probe_plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv,
     out[4] = p.nsub;
     out[5] = p.wg_per_group;
     out[6] = p.grid;
+    out[7] = p.rows16;
+    out[8] = p.n_rb16;
+    out[9] = p.n_tasks16;
 }
 
 uint32_t probe_max_cus(void) { return attn::kMaxCus; }

@@ -894,6 +894,9 @@ PREFILL_SWEEP = [
     (200, 3, 1, 256), (100, 16, 8, 256), (450, 10, 5, 32), (97, 9, 9, 64),
     (1000, 28, 7, 128),
     (200, 6, 3, 96), (64, 2, 1, 96), (129, 4, 2, 160), (300, 8, 4, 192), (97, 6, 6, 224),
+    # 16-row blocks at head_dim 192 / 256: an odd count of 16-row blocks (the
+    # middle one alone), ragged ends, workgroups whose tasks span two pairs
+    (33, 2, 2, 256), (17, 3, 3, 192), (1000, 8, 4, 192), (1024, 16, 2, 256), (495, 14, 7, 192),
 ]
 
 

@@ -17,7 +17,8 @@ CSRC = os.path.join(ROOT, "attention_gqa_online_amd", "csrc")
 U64P = ctypes.POINTER(ctypes.c_uint64)
 DEC = ("head_chunk", "n_chunks", "units", "n_split", "rows_per_split", "w0", "g_target",
        "part_floats", "part_offset", "workspace_bytes")
-PRE = ("waves", "n_rb", "n_pairs", "zigzag", "nsub", "wg_per_group", "grid")
+PRE = ("waves", "n_rb", "n_pairs", "zigzag", "nsub", "wg_per_group", "grid", "rows16", "n_rb16",
+       "n_tasks16")
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +42,7 @@ def decode_plan(lib, b, hq, hkv, d, t, w, append=False, varlen=False, cus=256):
 
 
 def prefill_plan(lib, m, hq, hpk, d, cus=256):
-    out = (ctypes.c_uint64 * 7)()
+    out = (ctypes.c_uint64 * 10)()
     lib.probe_plan_prefill(m, hq, hpk, d, cus, out)
     return dict(zip(PRE, out))
 
@@ -120,7 +121,17 @@ def test_prefill_grid_follows_compute_units(probe):
     # Qwen-2.5-7B-shaped layer (28 Q / 4 KV heads, m 2048): under two
     # workgroups per compute unit, so short and long row blocks pair up
     p = prefill_plan(probe, 2048, 28, 7, 128, cus=256)
-    assert (p["zigzag"], p["nsub"], p["grid"], p["waves"]) == (1, 2, 256, 8)
+    assert (p["zigzag"], p["rows16"], p["nsub"], p["grid"], p["waves"]) == (1, 0, 2, 256, 8)
+    # head_dim 256 on such a grid: 16-row blocks, a pair per wave (64 pairs x
+    # 2 heads = 128 equal tasks per KV head, 8 per workgroup)
+    p = prefill_plan(probe, 2048, 16, 2, 256, cus=256)
+    assert (p["zigzag"], p["rows16"], p["waves"]) == (1, 1, 8)
+    assert (p["n_rb16"], p["n_tasks16"], p["grid"]) == (128, 128, 128)
+    # head_dim 224 (not a multiple of 64) keeps the 32-row zigzag kernel
+    assert prefill_plan(probe, 2048, 16, 2, 224, cus=256)["rows16"] == 0
+    # an odd number of 16-row blocks: the middle one pairs with itself
+    p = prefill_plan(probe, 40, 4, 2, 192, cus=256)
+    assert (p["rows16"], p["n_rb16"], p["n_tasks16"], p["grid"]) == (1, 3, 4, 2)
     # a quarter of the compute units: 224 row-block-major workgroups fill
     # them more than twice over
     p = prefill_plan(probe, 2048, 28, 7, 128, cus=64)
