@@ -694,19 +694,29 @@ extern "C" int read_two(int kind, const void *a, const void *b, size_t n4, unsig
 """
 
 
-def bench_read_ceiling(args, dev):
-    """Practical HBM read ceiling at the decode step's byte count: plain read
-    kernels (two buffers of 128 MiB per call, like the caches' K and V; three
-    such pairs in rotation), built with hipcc here."""
-    import ctypes
-    import torch
-    d = tempfile.mkdtemp(prefix="read_ceiling_")
-    src, so = os.path.join(d, "read_ceiling.hip"), os.path.join(d, "libread_ceiling.so")
+def build_read_ceiling(so: str) -> str:
+    """Compile the plain read kernels (READ_CEILING_SRC) with hipcc into `so`."""
+    os.makedirs(os.path.dirname(os.path.abspath(so)), exist_ok=True)
+    src = os.path.splitext(os.path.abspath(so))[0] + ".hip"
     with open(src, "w") as f:
         f.write(READ_CEILING_SRC)
     subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared",
                            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                            "-o", so, src], stderr=subprocess.DEVNULL)
+    return so
+
+
+def bench_read_ceiling(args, dev):
+    """Practical HBM read ceiling at the decode step's byte count: plain read
+    kernels (two buffers of 128 MiB per call, like the caches' K and V; three
+    such pairs in rotation), built with hipcc here unless --read-ceiling-so
+    names one built beforehand (--build-read-ceiling)."""
+    import ctypes
+    import torch
+    so = args.read_ceiling_so
+    if not so or not os.path.exists(so):
+        so = build_read_ceiling(so or os.path.join(tempfile.mkdtemp(prefix="read_ceiling_"),
+                                                   "libread_ceiling.so"))
     lib = ctypes.CDLL(so)
     lib.read_two.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                              ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
@@ -771,7 +781,14 @@ def main():
     ap.add_argument("--modes", default=DEFAULT_MODES,
                     help="comma list; the headline decode step always runs "
                          "(also: read_ceiling, copy_calibration)")
+    ap.add_argument("--read-ceiling-so", default=None,
+                    help="read_ceiling: the plain read kernels' library (built there if missing)")
+    ap.add_argument("--build-read-ceiling", default=None, metavar="SO",
+                    help="only build the read_ceiling library at SO (no GPU use), then exit")
     args = ap.parse_args()
+    if args.build_read_ceiling:
+        print(build_read_ceiling(args.build_read_ceiling))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU code; each GPU would run its own share)",
