@@ -62,7 +62,9 @@ __all__ = [
     "attn_status_string", "decode_workspace",
 ]
 
-SO_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_GQA_LIB names another build of the library (an instrumented one, say)
+SO_PATH = os.environ.get("ATTN_GQA_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 
