@@ -102,3 +102,53 @@ def test_noalloc_matches_the_workspace_step_on_calls_in_a_row():
         vmax = float(np.abs(vc[:, :, w.window_start:pos + 1]).max())
         err = float(np.abs(got.astype(np.float64) - ref).max())
         assert err <= TOL * vmax, f"{case}: max|err| {err:.3e} > {TOL * vmax:.3e}"
+
+
+@pytest.mark.gpu
+def test_noalloc_step_replays_from_a_hip_graph():
+    """The no-allocation step captured in a HIP graph (the callers it is
+    for): every replay, with eager work between replays that includes an
+    eager no-allocation call of another shape on the same array, gives the
+    bits of the eager workspace step."""
+    import torch
+    dev = torch.device("cuda:0")
+    b, hq, hkv, d, ms, pos = 8, 12, 2, 128, 2100, 2047
+    w = synth.DecodeWorkload("noalloc_graph", batch=b, num_heads=hq, kv_heads=hkv, head_dim=d,
+                             max_seq=ms, total_seq=pos + 1, seed=71)
+    q, kc, vc = synth.decode_inputs(w)
+    kn, vn = synth.append_inputs(b, hkv, d, seed=72)
+    qd, kd, vd, knd, vnd = (torch.from_numpy(x).to(dev) for x in (q, kc, vc, kn, vn))
+    ws = A.decode_workspace(b, hq, hkv, d, pos + 1, 0, device=dev)
+    out_e = torch.empty(b, hq, d, device=dev)
+    A.attn_decode_append(qd, knd, vnd, kd, vd, out_e, b, hq, hkv, d, ms, pos, 0, w.scale, ws)
+    # another shape for the eager calls between replays
+    w2 = synth.DecodeWorkload("noalloc_other", batch=3, num_heads=8, kv_heads=2, head_dim=64,
+                              max_seq=900, total_seq=800, window=300, seed=73)
+    q2, k2, v2 = synth.decode_inputs(w2)
+    kn2, vn2 = synth.append_inputs(3, 2, 64, seed=74)
+    q2d, k2d, v2d, kn2d, vn2d = (torch.from_numpy(x).to(dev) for x in (q2, k2, v2, kn2, vn2))
+    out2_e = torch.empty(3, 8, 64, device=dev)
+    ws2 = A.decode_workspace(3, 8, 2, 64, 800, 300, device=dev)
+    A.attn_decode_append(q2d, kn2d, vn2d, k2d, v2d, out2_e, 3, 8, 2, 64, 900, 799, 300,
+                         w2.scale, ws2)
+    out_g = torch.empty(b, hq, d, device=dev)
+    out2_n = torch.empty(3, 8, 64, device=dev)
+    # a first call on this device looks up the array outside the capture
+    A.attn_decode_append_noalloc(qd, knd, vnd, kd, vd, out_g, b, hq, hkv, d, ms, pos, 0, w.scale)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.attn_decode_append_noalloc(qd, knd, vnd, kd, vd, out_g, b, hq, hkv, d, ms, pos, 0,
+                                     w.scale)
+    for rep in range(4):
+        print("noalloc graph replay", rep, flush=True)
+        out_g.fill_(float("nan"))
+        out2_n.fill_(float("nan"))
+        A.attn_decode_append_noalloc(q2d, kn2d, vn2d, k2d, v2d, out2_n, 3, 8, 2, 64, 900, 799,
+                                     300, w2.scale)
+        junk = torch.randn(1 << 20, device=dev).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep}"
+        assert torch.equal(out2_n, out2_e), f"eager call before replay {rep}"
+        assert bool(torch.isfinite(junk))
