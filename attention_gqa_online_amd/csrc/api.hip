@@ -1,7 +1,9 @@
 // C ABI of libattn.so (declared in include/attn.h): argument checks on the
 // host, then one kernel launch on the caller's stream. No check below makes a
-// HIP call, so an invalid call returns before touching the device; the only
-// HIP calls before a launch are the once-per-device compute-unit query.
+// HIP call, so an invalid call returns before touching the device. The only
+// HIP calls made before a launch, after the checks, are the compute-unit
+// query (hipGetDevice per call, the attribute once per device) and, for the
+// no-allocation decode step, the lookup of the scratch array (once per device).
 #include <math.h>
 #include <stdint.h>
 
