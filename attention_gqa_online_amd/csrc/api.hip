@@ -6,6 +6,7 @@
 // no-allocation decode step, the lookup of the scratch array (once per device).
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <atomic>
 #include <mutex>
@@ -18,6 +19,19 @@ namespace attn {
 namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<uint32_t> g_cus[kMaxDevices];  // 0: not queried yet
+
+// ATTN_GQA_CUS=n: plan for at most n compute units (read once; 0 if unset or
+// not a positive number).
+uint32_t env_cus_limit() {
+    static const uint32_t limit = [] {
+        const char *v = getenv("ATTN_GQA_CUS");
+        if (v == nullptr) return 0u;
+        char *end = nullptr;
+        const unsigned long n = strtoul(v, &end, 10);
+        return end != v && *end == '\0' && n > 0 && n <= kMaxCus ? (uint32_t)n : 0u;
+    }();
+    return limit;
+}
 }  // namespace
 
 uint32_t device_cus() {
@@ -31,7 +45,9 @@ uint32_t device_cus() {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
         return kMaxCus;
-    const uint32_t c = (uint32_t)n < kMaxCus ? (uint32_t)n : kMaxCus;
+    uint32_t c = (uint32_t)n < kMaxCus ? (uint32_t)n : kMaxCus;
+    const uint32_t limit = env_cus_limit();
+    if (limit != 0 && limit < c) c = limit;
     if (dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
     return c;
 }

@@ -37,7 +37,9 @@
  *     caller's next synchronisation. All argument checks run on the host
  *     before any HIP call, so an invalid call launches nothing. The work
  *     split follows the current device's compute-unit count, queried once
- *     per device and kept for the life of the process.
+ *     per device and kept for the life of the process; the environment
+ *     variable ATTN_GQA_CUS=n (read once) caps it at n, for a GPU shared
+ *     with other work. Results do not depend on it beyond fp32 rounding.
  *   - Outputs must not overlap inputs. Concurrent calls must not share an
  *     output buffer or a decode workspace.
  *   - Pointers must be 16-byte aligned; strides are in elements and must be
