@@ -507,7 +507,8 @@ def bench_prefill(args, dev, name, orc, clock=False):
                      else "back-to-back mean per call, median of 3 runs",
            "roofline": {"bound": "mfma", "achieved": round(tfl, 3),
                         "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tfl / FP32_MFMA_PEAK_TFLOPS, 4)},
+                        "frac": round(tfl / FP32_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic("attn_prefill_causal:" + name)},
            "algorithmic_flops": w.flops(), "launches_per_call": 1}
     log(f"[bench] {name}: {mean * 1e3:.1f} us per call back to back, per-call event median "
         f"{med * 1e3:.1f} us; {tfl:.2f} TFLOP/s")
