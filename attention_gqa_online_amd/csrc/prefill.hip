@@ -72,6 +72,23 @@ struct PrefillArgs {
     float qscale;          // (1/sqrt(d) in f32) * log2(e)
 };
 
+// max of three scores in one instruction. Written out because fmaxf on
+// matrix-core results is preceded by a canonicalising max per operand (the
+// compiler cannot assume they are quieted); scores here are finite or -inf.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max of lane l and lane l ^ 32: v_permlane32_swap exchanges the upper half
+// of its first operand with the lower half of its second, so with both equal
+// to x the two results hold x and its partner in every lane
+__device__ __forceinline__ float max_lane_pair(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -121,6 +138,41 @@ __device__ __forceinline__ void load_tile_lds(const PrefillArgs &a, uint32_t g, 
     }
 }
 
+// The same copy for a tile whose 64 rows all lie below m, for head sizes
+// whose row holds a power-of-two number of chunks (32, 64, 128). Instruction
+// i covers rows R_i .. R_i + 64 / CPR - 1 (R_i = (wave * NI + i) * 64 / CPR,
+// a multiple of 64 / CPR), so the swizzled chunk of lane l is
+// (l mod CPR) ^ ((l / CPR) mod SW) ^ (R_i mod SW): a per-lane constant lx
+// XOR a uniform value. The source is a uniform row address plus a 32-bit
+// per-lane offset (ly = the lane's row within the instruction, in bytes,
+// plus 16 * chunk): two vector instructions per copy.
+template <int D>
+constexpr bool kFastCopy = D == 32 || D == 64 || D == 128;
+
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_lds_full(const PrefillArgs &a, uint32_t g, uint32_t kt,
+                                                   float *sk, float *sv, int wave, uint32_t lx,
+                                                   uint32_t ly) {
+    constexpr int CPR = D / 4;
+    constexpr int NI = kBc * CPR / (NW * 64);
+    constexpr int SW = swz_width(D);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const uint32_t ri = (uint32_t)(wave * NI + i) * (64 / CPR);  // uniform
+        const size_t row0 = ((size_t)kt * kBc + ri) * a.kv_stride + (size_t)g * D;
+        const uint32_t off = ly + 16u * (lx ^ (ri & (SW - 1)));
+        const char *kb = reinterpret_cast<const char *>(a.k + row0);
+        const char *vb = reinterpret_cast<const char *>(a.v + row0);
+        const int loff = (wave * NI + i) * 64 * 4;  // floats; lane offset added by hardware
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(kb + off),
+            (__attribute__((address_space(3))) void *)(sk + loff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(vb + off),
+            (__attribute__((address_space(3))) void *)(sv + loff), 16, 0, 0);
+    }
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     constexpr int HW = NW / 2;  // zigzag: waves per row block of the pair
@@ -150,8 +202,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         // u, the second half the same heads of block n_rb-1-u, so each SIMD
         // runs one short and one long wave (8 waves) and every workgroup has
         // about the same work
+        //
+        // The sub-workgroup index of a pair is rotated by a term that grows
+        // with u, so that workgroups with fewer heads (the last sub-workgroup
+        // when heads_per_kv is not a multiple of NW / 2) are spread over the
+        // XCDs instead of all landing on the XCDs (blockIdx mod 8) of one
+        // parity: an XCD whose compute units all run four busy SIMDs ends
+        // later than one that runs three. gx = gcd(8, kv_heads); over the
+        // blocks of one XCD, u / (8 / (nsub * gx)) steps once per such
+        // period. Within a pair's nsub workgroups it is a rotation, so every
+        // (u, sub) is still taken exactly once.
         const uint32_t u = wi / a.nsub;
-        hl = (wi % a.nsub) * HW + (wave % HW);
+        const uint32_t gx = min(a.kv_heads & (~a.kv_heads + 1u), 8u);
+        const uint32_t sub = (wi % a.nsub + u * a.nsub * gx / 8) % a.nsub;
+        hl = sub * HW + (wave % HW);
         const uint32_t lo = u, hi = a.n_rb - 1 - u;
         rb = wave < HW ? lo : hi;
         active = hl < a.hpk && (wave < HW || hi > lo);
@@ -175,7 +239,24 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const uint32_t my_kend = active ? min(qr0 + kBr, a.m) : 0;
     const uint32_t my_ntiles = (my_kend + kBc - 1) / kBc;
 
-    load_tile_lds<D, NW>(a, g, 0, sK0, sV0, wave, lane);
+    // tiles whose rows all lie below m take the cheaper copy when its 32-bit
+    // per-lane offsets hold (a tile's rows span under 4 GiB: kv_stride < 2^24)
+    constexpr int CPR = D / 4;
+    const uint32_t lx = (uint32_t)((lane % CPR) ^ ((lane / CPR) & (swz_width(D) - 1)));
+    const uint32_t ly = (uint32_t)(lane / CPR) * a.kv_stride * 4u;
+    const uint32_t nfull = kFastCopy<D> && a.kv_stride < (1u << 24) ? a.m / kBc : 0;
+    auto load_tile = [&](uint32_t kt, float *sk, float *sv) __attribute__((always_inline)) {
+        if (kFastCopy<D> && kt < nfull) {
+            // opaque per copy: the offsets are formed here, not hoisted out
+            // of the tile loop and held in registers
+            uint32_t x = lx, y = ly;
+            asm volatile("" : "+v"(x), "+v"(y));
+            load_tile_lds_full<D, NW>(a, g, kt, sk, sv, wave, x, y);
+        } else {
+            load_tile_lds<D, NW>(a, g, kt, sk, sv, wave, lane);
+        }
+    };
+    load_tile(0, sK0, sV0);
 
     // Q^T operand: lane (j, half) holds Q[qi][8u + 4half + 0..3] for u < D/8
     float4 qt[NQ];
@@ -260,10 +341,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
             }
 
             // online softmax for query row qi (this lane and lane ^ 32 share it)
-            float mx = kNegInf;
+            // two chains of v_max3 over the 32 scores (no canonicalising of
+            // the MFMA results, which fmaxf would add), then the partner
+            // lane's maximum through a lane-half swap
+            float ma = vmax3(s0[0], s0[1], s1[0]), mb = vmax3(s1[1], s0[2], s1[2]);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            for (int e = 3; e < 15; e += 2) {
+                ma = vmax3(ma, s0[e], s1[e]);
+                mb = vmax3(mb, s0[e + 1], s1[e + 1]);
+            }
+            ma = vmax3(ma, s0[15], s1[15]);
+            float mx = fmaxf(ma, mb);
+            mx = max_lane_pair(mx);
             // The reference max is raised (and O, l rescaled) only when some
             // row of the wave sees a score more than kLazyRescale above it;
             // otherwise the weights 2^(s - m) stay below 2^kLazyRescale and
@@ -342,12 +431,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         for (uint32_t kt = 0; kt < ntiles; kt += 2) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
             __syncthreads();  // every wave's loads landed; buffer 1 is free
-            if (kt + 1 < ntiles) load_tile_lds<D, NW>(a, g, kt + 1, sK1, sV1, wave, lane);
+            if (kt + 1 < ntiles) load_tile(kt + 1, sK1, sV1);
             tile(sK0, sV0, kt);
             if (kt + 1 >= ntiles) break;
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();  // buffer 0 is free
-            if (kt + 2 < ntiles) load_tile_lds<D, NW>(a, g, kt + 2, sK0, sV0, wave, lane);
+            if (kt + 2 < ntiles) load_tile(kt + 2, sK0, sV0);
             tile(sK1, sV1, kt + 1);
         }
     } else {
@@ -357,7 +446,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
             tile(sK0, sV0, kt);
             if (kt + 1 < ntiles) {
                 __syncthreads();  // single buffer: everyone done before it is refilled
-                load_tile_lds<D, NW>(a, g, kt + 1, sK0, sV0, wave, lane);
+                load_tile(kt + 1, sK0, sV0);
             }
         }
     }
@@ -549,13 +638,18 @@ __global__ __launch_bounds__(512) void prefill16_kernel(PrefillArgs a) {
         }
         // online softmax for row qi: its 64 scores sit in lanes j, j+16,
         // j+32, j+48, 16 each; every processed tile has an unmasked key per row
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
+        // v_max3 over the 16 scores (as in prefill_kernel), then the other
+        // lane groups of the row
+        float mx = vmax3(s[0][0], s[0][1], s[0][2]);
+        mx = vmax3(mx, s[0][3], s[1][0]);
+        mx = vmax3(mx, s[1][1], s[1][2]);
+        mx = vmax3(mx, s[1][3], s[2][0]);
+        mx = vmax3(mx, s[2][1], s[2][2]);
+        mx = vmax3(mx, s[2][3], s[3][0]);
+        mx = vmax3(mx, s[3][1], s[3][2]);
+        mx = fmaxf(mx, s[3][3]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_lane_pair(mx);
         if (__any(mx > mrow + kLazyRescale)) {  // wave-uniform, as in prefill_kernel
             const float mnew = fmaxf(mrow, mx);
             const float cf = fast_exp2(mrow - mnew);
