@@ -45,8 +45,10 @@
 namespace attn {
 namespace {
 
-// Waves per workgroup: 8 (two per SIMD, so one wave's softmax runs under the
-// other's matrix work), or, for head_dim >= 192 on grids that fill the chip
+// Waves per workgroup: 8 (two per SIMD, so one wave's matrix work fills the
+// other's waits on LDS reads, barriers and dependent instructions; vector
+// instructions themselves do not run under fp32 MFMAs, whichever wave issues
+// them), or, for head_dim >= 192 on grids that fill the chip
 // twice, 4: there Q^T and the O^T accumulators of a 32-row block alone take
 // head_dim registers, and with one wave per SIMD a lane has 512 registers
 // instead of 256, so nothing goes to scratch memory. (On smaller grids the
@@ -295,8 +297,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
             int xh = (j & (SW - 1)) ^ half;
             asm volatile("" : "+v"(xh));
             const float *krow = sk + j * D;
-            // a wave in a matrix phase gets issue priority, so the SIMD's
-            // other wave fills the MFMA pipe's gaps with its vector work
+            // a wave in a matrix phase gets issue priority (measured faster;
+            // vector instructions do not run under fp32 MFMAs here, so this
+            // orders the two waves' issue rather than hiding the softmax)
             __builtin_amdgcn_s_setprio(1);
             float4 ka[2], kb[2];
             ka[0] = ld4(krow + 4 * xh);
