@@ -75,6 +75,12 @@ PrefillPlan plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv
                          uint32_t head_dim, uint32_t cus) {
     PrefillPlan p{};
     if (heads_per_kv == 0) return p;
+    if (m <= (uint32_t)kSmallRows) {
+        p.small = 1;
+        p.waves = 4;
+        p.grid = (num_q_heads + 3) / 4;
+        return p;
+    }
     cus = clamp_cus(cus);
     const uint32_t kv_heads = num_q_heads / heads_per_kv;
     p.n_rb = (m + kPrefillRows - 1) / kPrefillRows;

@@ -83,8 +83,11 @@ DecodePlan plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
 // ---------------------------------------------------------------- prefill
 constexpr int kPrefillRows = 32;       // query rows per wave (one MFMA block)
 constexpr int kMinDim4Waves = 192;     // head_dim from which large grids use 4-wave workgroups
+constexpr int kSmallRows = 16;         // m up to this: one wave per Q head, no LDS (small)
 
-// Grid of one prefill call. Workgroups of `waves` waves share one KV head;
+// Grid of one prefill call. Prompts of at most kSmallRows rows take the
+// small kernel (one wave per Q head reads its Q, K and V rows straight into
+// registers). Otherwise workgroups of `waves` waves share one KV head;
 // row-block-major (wave w of workgroup i owns (row block, head) pair
 // i*waves + w of its group), or, on grids under two workgroups per compute
 // unit, zigzag (the first half of the waves take row block u, the second
@@ -104,6 +107,9 @@ struct PrefillPlan {
     uint32_t rows16;        // 1: the 16-row kernel (then the fields below)
     uint32_t n_rb16;        // ceil(m / 16)
     uint32_t n_tasks16;     // ceil(n_rb16 / 2) * heads_per_kv per KV head
+    uint32_t small;         // 1: m <= kSmallRows, one wave per Q head in 4-wave
+                            // workgroups (grid = ceil(num_q_heads / 4)); the
+                            // fields above are then unused
 };
 
 PrefillPlan plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv,

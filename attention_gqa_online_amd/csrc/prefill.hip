@@ -91,6 +91,16 @@ __device__ __forceinline__ float max_lane_pair(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// sum of lane l and lane l ^ 32 (the same exchange as max_lane_pair)
+__device__ __forceinline__ float sum_lane_pair(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -747,9 +757,124 @@ __global__ __launch_bounds__(512) void prefill16_kernel(PrefillArgs a) {
     finish();  // the second blocks (or the first, in a workgroup without second blocks)
 }
 
+// ---------------------------------------------------------------------------
+// Prompts of at most kSmallRows (16) rows: one wave per Q head h computes the
+// whole problem on v_mfma_f32_16x16x4_f32 with its operands read straight
+// from global memory into registers (no LDS, no barrier; each head of a KV
+// group reads the group's few K and V rows, from L2 after the first).
+// Lane l = (i, kk), i = l % 16, kk = l / 16. Operand layouts of 16x16x4: lane
+// l supplies A[i][kk] and B[kk][i] and receives C[4kk + v][i] in register v.
+//   S^T[key][row] = sum_d K[key][d] Q[row][d]: k-step s of lane group kk
+//     contracts d = kk * D/4 + s, so a lane reads D/4 consecutive floats of
+//     its K row and of its Q row (row i; rows past m re-read row m - 1).
+//   Lane (i, kk) then holds the scores of keys 4kk + v for row i; keys above
+//     the row (which include those past m) are masked, and the row's maximum
+//     and sum combine the four lane groups with two exchanges. Key 0 is never
+//     masked, so every maximum is finite.
+//   O^T[d][row] += V^T[d][key] P^T[key][row] for output blocks b: A row i' is
+//     d = b + (D/16) i', and k-step t of lane group kk takes key 4kk + t, so
+//     the B operand is register t of the score accumulator and a lane reads
+//     D/16 consecutive floats of V row 4kk + t per k-step.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_small_kernel(PrefillArgs a) {
+    constexpr int NS = D / 4;   // QK^T k-steps per lane group
+    constexpr int NB = D / 16;  // 16-row blocks of O^T = floats of a V row per lane
+    static_assert(NS % 4 == 0 && NB % 2 == 0, "whole float4 / float2 reads");
+    const int lane = threadIdx.x & 63;
+    const uint32_t h = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (h >= a.kv_heads * a.hpk) return;  // wave-uniform: past the last head
+    const uint32_t g = h / a.hpk;
+    const int i = lane & 15, kk = lane >> 4;
+    const uint32_t r = min((uint32_t)i, a.m - 1);  // this lane's Q row and K row
+
+    // V operands first: nothing they feed depends on the scores' arrival
+    float vv[4][NB];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t rv = min((uint32_t)(4 * kk + t), a.m - 1);
+        const float *vrow = a.v + (size_t)rv * a.kv_stride + (size_t)g * D + NB * i;
+        if constexpr (NB % 4 == 0) {
+#pragma unroll
+            for (int c = 0; c < NB / 4; ++c) {
+                const float4 x = ld4(vrow + 4 * c);
+                vv[t][4 * c] = x.x; vv[t][4 * c + 1] = x.y;
+                vv[t][4 * c + 2] = x.z; vv[t][4 * c + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NB / 2; ++c) {
+                const float2 x = *reinterpret_cast<const float2 *>(vrow + 2 * c);
+                vv[t][2 * c] = x.x; vv[t][2 * c + 1] = x.y;
+            }
+        }
+    }
+
+    const float *qrow = a.q + (size_t)r * a.q_stride + (size_t)h * D + kk * NS;
+    const float *krow = a.k + (size_t)r * a.kv_stride + (size_t)g * D + kk * NS;
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NS / 4; ++c) {
+        const float4 q4 = ld4(qrow + 4 * c) * a.qscale;
+        const float4 k4 = ld4(krow + 4 * c);
+        s = mfma16(k4.x, q4.x, s);
+        s = mfma16(k4.y, q4.y, s);
+        s = mfma16(k4.z, q4.z, s);
+        s = mfma16(k4.w, q4.w, s);
+    }
+
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        if (4 * kk + v > i) s[v] = kNegInf;
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = max_lane_pair(mx);
+    float p[4], l = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        p[v] = fast_exp2(s[v] - mx);
+        l += p[v];
+    }
+    l += __shfl_xor(l, 16);
+    l = sum_lane_pair(l);
+
+    floatx4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma16(vv[t][b], p[t], acc[b]);
+
+    // register v of block b is O[i][b + NB (4kk + v)]: NB consecutive floats per v
+    if ((uint32_t)i < a.m) {
+        const float inv = 1.0f / l;
+        float *orow = a.o + (size_t)i * a.q_stride + (size_t)h * D;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float *op = orow + NB * (4 * kk + v);
+            if constexpr (NB % 4 == 0) {
+#pragma unroll
+                for (int c = 0; c < NB / 4; ++c)
+                    *reinterpret_cast<float4 *>(op + 4 * c) =
+                        make_float4(acc[4 * c][v] * inv, acc[4 * c + 1][v] * inv,
+                                    acc[4 * c + 2][v] * inv, acc[4 * c + 3][v] * inv);
+            } else {
+#pragma unroll
+                for (int c = 0; c < NB / 2; ++c)
+                    *reinterpret_cast<float2 *>(op + 2 * c) =
+                        make_float2(acc[2 * c][v] * inv, acc[2 * c + 1][v] * inv);
+            }
+        }
+    }
+}
+
 template <int D>
 hipError_t launch_d(const PrefillArgs &args, uint32_t grid, uint32_t nw, bool rows16,
-                    hipStream_t stream) {
+                    bool small, hipStream_t stream) {
+    if (small) {
+        hipLaunchKernelGGL((prefill_small_kernel<D>), dim3(grid), dim3(256), 0, stream, args);
+        return hipGetLastError();
+    }
     if constexpr (D >= kMinDim4Waves && D % 64 == 0) {  // the plan's rows16 head sizes
         if (rows16) {
             hipLaunchKernelGGL((prefill16_kernel<D>), dim3(grid), dim3(8 * 64), 0, stream, args);
@@ -791,16 +916,16 @@ hipError_t launch_prefill(const PrefillPlan &plan, const float *q, const float *
     a.n_tasks16 = plan.n_tasks16;
     a.qscale = (1.0f / sqrtf((float)head_dim)) * kLog2e;
     const uint32_t grid = plan.grid, nw = plan.waves;
-    const bool r16 = plan.rows16 != 0;
+    const bool r16 = plan.rows16 != 0, sm = plan.small != 0;
     switch (head_dim) {
-    case 32: return launch_d<32>(a, grid, nw, r16, stream);
-    case 64: return launch_d<64>(a, grid, nw, r16, stream);
-    case 96: return launch_d<96>(a, grid, nw, r16, stream);
-    case 128: return launch_d<128>(a, grid, nw, r16, stream);
-    case 160: return launch_d<160>(a, grid, nw, r16, stream);
-    case 192: return launch_d<192>(a, grid, nw, r16, stream);
-    case 224: return launch_d<224>(a, grid, nw, r16, stream);
-    case 256: return launch_d<256>(a, grid, nw, r16, stream);
+    case 32: return launch_d<32>(a, grid, nw, r16, sm, stream);
+    case 64: return launch_d<64>(a, grid, nw, r16, sm, stream);
+    case 96: return launch_d<96>(a, grid, nw, r16, sm, stream);
+    case 128: return launch_d<128>(a, grid, nw, r16, sm, stream);
+    case 160: return launch_d<160>(a, grid, nw, r16, sm, stream);
+    case 192: return launch_d<192>(a, grid, nw, r16, sm, stream);
+    case 224: return launch_d<224>(a, grid, nw, r16, sm, stream);
+    case 256: return launch_d<256>(a, grid, nw, r16, sm, stream);
     default: return hipErrorInvalidValue;
     }
 }

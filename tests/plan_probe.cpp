@@ -29,7 +29,7 @@ void probe_plan_decode(uint32_t batch, uint32_t num_heads, uint32_t kv_heads,
 }
 
 // out: waves, n_rb, n_pairs, zigzag, nsub, wg_per_group, grid, rows16, n_rb16,
-// n_tasks16
+// n_tasks16, small
 void probe_plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv,
                         uint32_t head_dim, uint32_t cus, uint64_t *out) {
     const attn::PrefillPlan p =
@@ -44,6 +44,7 @@ void probe_plan_prefill(uint32_t m, uint32_t num_q_heads, uint32_t heads_per_kv,
     out[7] = p.rows16;
     out[8] = p.n_rb16;
     out[9] = p.n_tasks16;
+    out[10] = p.small;
 }
 
 uint32_t probe_max_cus(void) { return attn::kMaxCus; }

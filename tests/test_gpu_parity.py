@@ -897,6 +897,10 @@ PREFILL_SWEEP = [
     # 16-row blocks at head_dim 192 / 256: an odd count of 16-row blocks (the
     # middle one alone), ragged ends, workgroups whose tasks span two pairs
     (33, 2, 2, 256), (17, 3, 3, 192), (1000, 8, 4, 192), (1024, 16, 2, 256), (495, 14, 7, 192),
+    # up to 16 rows: one wave per Q head, every built head size, head counts
+    # that leave the last 4-wave workgroup part empty
+    (16, 8, 4, 128), (5, 3, 3, 256), (1, 2, 2, 96), (16, 16, 8, 160), (9, 7, 7, 224),
+    (12, 6, 2, 192), (3, 64, 8, 64), (16, 28, 7, 128), (7, 5, 1, 32),
 ]
 
 

@@ -18,7 +18,7 @@ U64P = ctypes.POINTER(ctypes.c_uint64)
 DEC = ("head_chunk", "n_chunks", "units", "n_split", "rows_per_split", "w0", "g_target",
        "part_floats", "part_offset", "workspace_bytes")
 PRE = ("waves", "n_rb", "n_pairs", "zigzag", "nsub", "wg_per_group", "grid", "rows16", "n_rb16",
-       "n_tasks16")
+       "n_tasks16", "small")
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +42,7 @@ def decode_plan(lib, b, hq, hkv, d, t, w, append=False, varlen=False, cus=256):
 
 
 def prefill_plan(lib, m, hq, hpk, d, cus=256):
-    out = (ctypes.c_uint64 * 10)()
+    out = (ctypes.c_uint64 * 11)()
     lib.probe_plan_prefill(m, hq, hpk, d, cus, out)
     return dict(zip(PRE, out))
 
@@ -143,3 +143,16 @@ def test_prefill_grid_follows_compute_units(probe):
     assert prefill_plan(probe, 8192, 32, 4, 256, cus=256)["waves"] == 4
     assert prefill_plan(probe, 1024, 32, 8, 256, cus=256)["waves"] == 8
     assert prefill_plan(probe, 1024, 32, 8, 256, cus=32)["waves"] == 4
+
+
+@pytest.mark.parametrize("m,hq,small,grid", [(1, 4, 1, 1), (16, 4, 1, 1), (16, 28, 1, 7), (5, 9, 1, 3),
+                                             (17, 4, 0, None)])
+def test_small_prompts_take_one_wave_per_head(probe, m, hq, small, grid):
+    """Up to 16 rows: the small kernel, one wave per Q head in 4-wave
+    workgroups, whatever the compute-unit count; 17 rows and up: the tiled
+    kernel."""
+    for cus in (256, 32):
+        p = prefill_plan(probe, m, hq, 1, 128, cus=cus)
+        assert p["small"] == small
+        if small:
+            assert (p["grid"], p["waves"]) == (grid, 4)
