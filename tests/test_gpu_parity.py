@@ -1151,6 +1151,32 @@ def test_prefill_past_two_gib_of_q(dev):
     _assert_close(got, ref, float(np.abs(vn).max()), "m 65536")
 
 
+@pytest.mark.parametrize("kvs", [(1 << 24) - 4, 1 << 24], ids=["fast_copy_edge", "general_copy"])
+def test_prefill_kv_stride_at_the_copy_offset_limit(dev, kvs):
+    """K/V rows 2^24 - 4 or 2^24 floats apart (about 8.7 GB per tensor at 130
+    rows): full tiles are copied with 32-bit per-lane offsets only below
+    2^24, so the first case takes that copy near its widest span (head_dim
+    32: 8 rows per copy instruction) and the second every tile the general
+    copy. The same rows at a compact stride go to the oracle."""
+    m, hq, hpk, d = 130, 2, 2, 32
+    w = synth.PrefillWorkload("kvs", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d, kv_stride=d, seed=71)
+    q, k, v = synth.prefill_inputs_device(w, 71, dev)
+    kb = torch.full((m, kvs), float("nan"), device=dev)
+    vb = torch.full((m, kvs), float("nan"), device=dev)
+    kb[:, :d] = k
+    vb[:, :d] = v
+    o = torch.full((m, hq * d), float("nan"), device=dev)
+    A.attn_prefill_causal(q, kb, vb, o, m, hq * d, kvs, hq, hpk, d)
+    torch.cuda.synchronize()
+    got = o.cpu().numpy()
+    del kb, vb
+    torch.cuda.empty_cache()
+    qn, kn, vn = q.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    ref = oracle.prefill_causal(qn, kn, vn, m, hq * d, d, hq, hpk, d)
+    _assert_close(got.reshape(ref.shape), ref, float(np.abs(vn).max()), f"kv_stride {kvs}")
+
+
 @pytest.mark.parametrize("per_tile,m", [(6.0, 700), (9.0, 700), (25.0, 256)])
 def test_prefill_rising_scores(dev, per_tile, m):
     """Scores that rise along the keys by `per_tile` log2 units per 64 keys
