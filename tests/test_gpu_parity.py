@@ -144,6 +144,33 @@ def test_decode_sweep(dev, case):
     _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), str(case))
 
 
+def _random_decode_shapes(n, seed):
+    """Seeded decode shapes: head sizes, GQA ratios (including ones that take
+    two head chunks), batch, cache lengths, attended lengths and windows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 96, 128, 160, 192, 224, 256]))
+        hkv = int(rng.integers(1, 5))
+        hpk = int(rng.choice([1, 2, 3, 4, 6, 8, 9, 12, 16]))
+        b = int(rng.integers(1, 7))
+        max_seq = int(rng.integers(1, 3000))
+        t = int(rng.integers(1, max_seq + 1))
+        window = 0 if rng.random() < 0.5 else int(rng.integers(1, t + 10))
+        out.append((b, hkv * hpk, hkv, d, max_seq, t, window))
+    return out
+
+
+DECODE_RANDOM = _random_decode_shapes(24, 4048)
+
+
+@pytest.mark.parametrize("case", DECODE_RANDOM, ids=lambda c: "b{}_hq{}_hkv{}_d{}_ms{}_t{}_w{}".format(*c))
+def test_decode_random_shapes(dev, case):
+    w, (q, k, v) = _decode_case(*case, seed=sum(case) % 997)
+    got = _gpu_decode(dev, w, q, k, v)
+    _assert_close(got, _ref_decode(w, q, k, v), _vmax_decode(w, v), str(case))
+
+
 def test_decode_spiky_window(dev):
     """N(0, 0.5) values with 1% of K rows x8 over all positions: the
     out-of-window spikes must not leak in, in-window ones stress the max."""
@@ -912,6 +939,36 @@ def test_prefill_sweep(dev, case):
     q, k, v = synth.prefill_inputs(w)
     o = _gpu_prefill(dev, w, q, k, v)
     _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), _vmax_prefill(w, v), str(case))
+
+
+def _random_prefill_shapes(n, seed):
+    """Seeded shapes across the built head sizes, GQA ratios, prompt lengths on
+    both sides of the small-prompt limit, and row strides with padding."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 96, 128, 160, 192, 224, 256]))
+        hkv = int(rng.integers(1, 4))
+        hpk = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8]))
+        m = int(rng.integers(1, 17)) if rng.random() < 0.3 else int(rng.integers(17, 300))
+        out.append((m, hkv * hpk, hpk, d, 4 * int(rng.integers(0, 3)), 4 * int(rng.integers(0, 3))))
+    return out
+
+
+PREFILL_RANDOM = _random_prefill_shapes(24, 2024)
+
+
+@pytest.mark.parametrize("case", PREFILL_RANDOM,
+                         ids=lambda c: "m{}_hq{}_hpk{}_d{}_qpad{}_kvpad{}".format(*c))
+def test_prefill_random_shapes(dev, case):
+    m, hq, hpk, d, qpad, kvpad = case
+    w = synth.PrefillWorkload("rand", m=m, num_q_heads=hq, heads_per_kv=hpk, head_dim=d,
+                              q_stride=hq * d + qpad, kv_stride=(hq // hpk) * d + kvpad,
+                              seed=m * 31 + hq * 7 + d)
+    q, k, v = synth.prefill_inputs(w)
+    o = _gpu_prefill(dev, w, q, k, v)
+    _assert_close(_heads(w, o), _ref_prefill(w, q, k, v), _vmax_prefill(w, v), str(case))
+    assert np.isnan(o[:, hq * d:]).all(), "padding columns of O were written"
 
 
 def test_prefill_fused_qkv_buffer(dev):
