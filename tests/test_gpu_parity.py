@@ -305,6 +305,27 @@ DECODE_APPEND_CASES = [
 ]
 
 
+def _random_step_shapes(n, seed):
+    """Seeded (batch, hq, hkv, d, max_seq, position or length bound, window)
+    cases for the fused decode steps."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 96, 128, 160, 192, 224, 256]))
+        hkv = int(rng.integers(1, 5))
+        hpk = int(rng.choice([1, 2, 3, 4, 6, 8, 9, 12]))
+        b = int(rng.integers(1, 9))
+        ms = int(rng.integers(1, 2500))
+        pos = int(rng.integers(0, ms))
+        win = 0 if rng.random() < 0.5 else int(rng.integers(1, pos + 12))
+        out.append((b, hkv * hpk, hkv, d, ms, pos, win))
+    return out
+
+
+# seeded random cases beside the hand-picked ones
+DECODE_APPEND_CASES = DECODE_APPEND_CASES + _random_step_shapes(16, 8096)
+
+
 def _decode_append_case(dev, case, seed):
     b, hq, hkv, d, ms, pos, win = case
     w, (q, k, v) = _decode_case(b, hq, hkv, d, ms, pos + 1, window=win, seed=seed)
@@ -670,7 +691,7 @@ VARLEN_APPEND_CASES = [
     (64, 8, 4, 128, 200, 160, 0),
     (32, 12, 2, 128, 4096, 4096, 0),
     (20, 4, 2, 32, 64, 64, 0),           # 40 units: more than one 32-lane merge wave's table
-]
+] + [(b, hq, hkv, d, ms, pos + 1, win) for (b, hq, hkv, d, ms, pos, win) in _random_step_shapes(12, 16192)]
 
 
 @pytest.mark.parametrize("case", VARLEN_APPEND_CASES,
